@@ -1,0 +1,143 @@
+/*
+ * qvae.h -- C ABI of the W8A8 INT8 CausalConv3d library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method (page "ComfyUI-Qwen-VAE-Triton v0.2.0: Triton W8A8 kernel
+ * accelerates the Qwen Image VAE decoder", sd114.wiki):
+ *   - intro paragraph: an implicit-GEMM W8A8 kernel for the CausalConv3d
+ *     layers of the Qwen-Image / Wan VAE decoder;
+ *   - section "Three presets explained", scheme paragraph: symmetric INT8
+ *     weights with one scale per output channel, dynamic symmetric INT8
+ *     activations, INT8 x INT8 products with INT32 accumulation, FP32
+ *     rescale, output in the activation's precision;
+ *   - same section, fixed-parameter paragraph: clip ratio 1.0 for activations
+ *     and weights, channels_last layout, automatic fallback to native
+ *     precision on error.
+ * Readings where the page is silent: the activation scale is one scale per
+ * tensor, s = fl(clip * absmax) / 127; codes are round-half-to-even of the
+ * IEEE float32 quotient x / s, clamped to [-127, 127] (0 when s == 0); the
+ * epilogue is y = bf16_rne(fma(float(acc), fl(s_x * s_w[co]), bias[co]));
+ * causality is kt-1 zero front frames, or an explicit int8 cache of the
+ * kt-1 previous frames quantized with the same scale.
+ *
+ * Conventions for every call:
+ *   - pointers are DEVICE pointers (memory from hipMalloc / a torch CUDA
+ *     tensor) unless stated otherwise; the caller allocates and frees every
+ *     buffer, the library allocates nothing and keeps no per-call state;
+ *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and never synchronize with the host;
+ *   - layouts are channels-last: activations [N][T][H][W][C], contiguous;
+ *   - x, xq, y, acc and cache must be 16-byte aligned;
+ *   - the return value is a status code (QVAE_OK = 0, negative on error);
+ *     arguments are validated before anything is launched; the library never
+ *     aborts or throws; on a non-zero status the caller is expected to fall
+ *     back to its native-precision path;
+ *   - setting the environment variable QVAE_FORCE_FAIL=1 makes every call
+ *     return QVAE_EFORCED without launching anything (to exercise the
+ *     caller's fallback);
+ *   - concurrent calls on different streams are safe as long as their output
+ *     buffers do not alias.
+ */
+#ifndef QVAE_H
+#define QVAE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QVAE_OK 0
+#define QVAE_EINVAL (-1)       /* null pointer, bad size, misaligned buffer   */
+#define QVAE_EUNSUPPORTED (-2) /* valid but outside the supported set          */
+#define QVAE_ELAUNCH (-3)      /* the HIP runtime reported a launch error      */
+#define QVAE_EFORCED (-4)      /* QVAE_FORCE_FAIL=1 is set                     */
+
+/* Library version, (major << 16) | minor. */
+int qvae_version(void);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char *qvae_strerror(int status);
+
+/*
+ * Weight quantization, once per layer at load time (scheme paragraph:
+ * symmetric INT8 weights, one scale per output channel; fixed parameters:
+ * weight clip ratio 1.0).
+ *   w        float32 [Cout][Cin][kt][kh][kw]  (the usual Conv3d weight layout)
+ *   wq       int8    [Cout][kt][kh][kw][Cin]  out (K-contiguous per channel)
+ *   w_scale  float32 [Cout]                   out
+ * w_scale[co] = fl(clip * max |w[co,...]|) / 127, the maximum taken over
+ * every (ci, kt, kh, kw); wq = clamp(rne(w / w_scale[co]), -127, 127), 0 for
+ * an all-zero channel.
+ * Supported: clip_ratio == 1.0f, Cout, Cin >= 1, kt, kh, kw in {1, 3}.
+ */
+int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh,
+                          int kw, float clip_ratio, int8_t *wq,
+                          float *w_scale, void *stream);
+
+/*
+ * Dynamic activation absmax (scheme paragraph: dynamic symmetric INT8
+ * activations; the scale is per tensor).
+ *   x            bf16 bit patterns, numel elements (any layout)
+ *   absmax_bits  uint32 [1] out: the bf16 bit pattern of max |x| (0..0x7F7F)
+ * Inputs must be finite.  numel >= 1.
+ */
+int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax_bits,
+                    void *stream);
+
+/*
+ * Activation quantization with the scale derived on the device from
+ * absmax_bits (fixed parameters: activation clip ratio 1.0).
+ *   x_scale  float32 [1] out: s = fl(clip * absmax) / 127
+ *   xq       int8 [numel] out: clamp(rne(x / s), -127, 127), 0 when s == 0
+ * Supported: clip_ratio == 1.0f.
+ */
+int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
+                      const uint32_t *absmax_bits, float *x_scale, int8_t *xq,
+                      void *stream);
+
+/* qvae_act_absmax followed by qvae_act_quantize on the same stream. */
+int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
+                          uint32_t *absmax_bits, float *x_scale, int8_t *xq,
+                          void *stream);
+
+/*
+ * W8A8 causal 3-D convolution as an implicit GEMM (intro paragraph: the
+ * implicit-GEMM kernel for CausalConv3d; scheme paragraph: INT8 x INT8 with
+ * INT32 accumulation, FP32 rescale, output in the activation precision).
+ *   xq       int8 [N][T][H][W][Cin]
+ *   x_scale  float32 [1] (device; from qvae_act_quantize)
+ *   cache    int8 [N][kt-1][H][W][Cin], the kt-1 frames before frame 0, oldest
+ *            first, quantized with the same x_scale; NULL = zero front frames
+ *   wq, w_scale  from qvae_quantize_weights
+ *   bias     float32 [Cout] or NULL (zero)
+ *   y        bf16 bit patterns [N][T][H][W][Cout] out
+ * y[n,t,h,w,co] = bf16_rne(fma(float(acc), fl(x_scale * w_scale[co]),
+ * bias[co])) with acc = sum over (i, j, l, ci) of
+ * wq[co,i,j,l,ci] * X(n, t-(kt-1)+i, h-(kh-1)/2+j, w-(kw-1)/2+l, ci), where
+ * frames before 0 come from the cache (or are zero) and out-of-image pixels
+ * are zero.  Stride 1, dilation 1, "same" spatial padding.
+ * Supported: Cin % 32 == 0, Cout % 32 == 0, kt in {1, 3}, (kh, kw) in
+ * {(1, 1), (3, 3)}, 127^2 * Cin * kt * kh * kw < 2^31.
+ */
+int qvae_causalconv3d_w8a8(const int8_t *xq, const float *x_scale,
+                           const int8_t *cache, const int8_t *wq,
+                           const float *w_scale, const float *bias, int N,
+                           int T, int H, int W, int Cin, int Cout, int kt,
+                           int kh, int kw, uint16_t *y, void *stream);
+
+/*
+ * Same contraction, writing the raw INT32 accumulators instead of the
+ * epilogue (a verification export):
+ *   acc  int32 [N][T][H][W][Cout] out
+ */
+int qvae_causalconv3d_w8a8_acc32(const int8_t *xq, const int8_t *cache,
+                                 const int8_t *wq, int N, int T, int H, int W,
+                                 int Cin, int Cout, int kt, int kh, int kw,
+                                 int32_t *acc, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QVAE_H */

@@ -82,9 +82,16 @@ static int8_t quantize_one(float v, float s)
 {
     if (s == 0.0f) return 0;          /* all-zero tensor or channel          */
     float t = v / s;                  /* one correctly rounded division      */
-    int32_t r = round_half_even(t);
-    if (r > 127) r = 127;
-    if (r < -127) r = -127;
+    int32_t r;
+    if (t >= 128.0f) {
+        r = 127;                      /* beyond the range: clamp (and keep   */
+    } else if (t <= -128.0f) {        /* the float -> int step in range)     */
+        r = -127;
+    } else {
+        r = round_half_even(t);
+        if (r > 127) r = 127;
+        if (r < -127) r = -127;
+    }
     return (int8_t)r;
 }
 

@@ -1,0 +1,137 @@
+"""The C-ABI boundary, without a GPU: the library loads, exports every entry
+point its header declares, and rejects bad arguments before launching
+anything (status codes, never an abort).  Also checks that the product
+package does not reach the oracle."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qvae.h")
+PKG = os.path.join(ROOT, "w8a8_int8_quantized_act_amd")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qvae_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from w8a8_int8_quantized_act_amd import ops
+    if not os.path.exists(ops.LIB_PATH):
+        from w8a8_int8_quantized_act_amd import build
+        build.build()
+    return ops.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["qvae_quantize_weights", "qvae_act_absmax", "qvae_act_quantize", "qvae_act_absmax_quant",
+              "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_acc32", "qvae_strerror", "qvae_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from w8a8_int8_quantized_act_amd import ops
+    out = subprocess.run(["nm", "-D", "--defined-only", ops.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        getattr(L, n)
+
+
+def test_version_and_strerror(L):
+    assert L.qvae_version() >= 1
+    for st in [0, -1, -2, -3, -4, 17]:
+        assert isinstance(L.qvae_strerror(st), bytes) and L.qvae_strerror(st)
+
+
+FAKE = ctypes.c_void_p(0x10000)        # aligned, never dereferenced: validation fails first
+FAKE_MIS = ctypes.c_void_p(0x10008)    # misaligned
+
+
+def conv(L, xq=FAKE, xs=FAKE, cache=None, wq=FAKE, ws=FAKE, b=None, dims=(1, 1, 4, 4, 32, 32, 3, 3, 3),
+         y=FAKE):
+    return L.qvae_causalconv3d_w8a8(xq, xs, cache, wq, ws, b, *dims, y, None)
+
+
+def test_conv_rejects_null_and_bad_sizes(L):
+    assert conv(L, xq=None) == -1
+    assert conv(L, y=None) == -1
+    assert conv(L, xs=None) == -1
+    assert conv(L, ws=None) == -1
+    assert conv(L, dims=(0, 1, 4, 4, 32, 32, 3, 3, 3)) == -1
+    assert conv(L, dims=(1, 1, -4, 4, 32, 32, 3, 3, 3)) == -1
+    assert conv(L, y=FAKE_MIS) == -1
+    assert conv(L, xq=FAKE_MIS) == -1
+
+
+def test_conv_rejects_unsupported(L):
+    assert conv(L, dims=(1, 1, 4, 4, 48, 32, 3, 3, 3)) == -2      # Cin % 32
+    assert conv(L, dims=(1, 1, 4, 4, 32, 40, 3, 3, 3)) == -2      # Cout % 32
+    assert conv(L, dims=(1, 1, 4, 4, 32, 32, 2, 3, 3)) == -2      # kt = 2
+    assert conv(L, dims=(1, 1, 4, 4, 32, 32, 3, 3, 1)) == -2      # kh != kw
+    assert conv(L, dims=(1, 1, 4, 4, 32, 32, 3, 5, 5)) == -2      # 5x5
+    assert conv(L, dims=(1, 1, 4, 4, 4960, 32, 3, 3, 3)) == -2    # 127^2 * K >= 2^31
+
+
+def test_acc32_rejects(L):
+    f = L.qvae_causalconv3d_w8a8_acc32
+    assert f(None, None, FAKE, 1, 1, 4, 4, 32, 32, 3, 3, 3, FAKE, None) == -1
+    assert f(FAKE, None, FAKE, 1, 1, 4, 4, 33, 32, 3, 3, 3, FAKE, None) == -2
+
+
+def test_quant_entry_points_reject(L):
+    assert L.qvae_act_absmax(None, 16, FAKE, None) == -1
+    assert L.qvae_act_absmax(FAKE, 0, FAKE, None) == -1
+    assert L.qvae_act_absmax(FAKE_MIS, 16, FAKE, None) == -1
+    assert L.qvae_act_quantize(FAKE, 16, 1.0, None, FAKE, FAKE, None) == -1
+    assert L.qvae_act_quantize(FAKE, 16, 0.5, FAKE, FAKE, FAKE, None) == -2   # clip != 1
+    assert L.qvae_act_absmax_quant(FAKE, 16, 1.0, FAKE, FAKE, FAKE_MIS, None) == -1
+    assert L.qvae_act_absmax_quant(FAKE, 16, 0.9, FAKE, FAKE, FAKE, None) == -2
+    assert L.qvae_quantize_weights(None, 32, 32, 3, 3, 3, 1.0, FAKE, FAKE, None) == -1
+    assert L.qvae_quantize_weights(FAKE, 32, 32, 3, 3, 3, 0.5, FAKE, FAKE, None) == -2
+    assert L.qvae_quantize_weights(FAKE, 32, 32, 2, 3, 3, 1.0, FAKE, FAKE, None) == -2
+
+
+def test_force_fail_hook():
+    # QVAE_FORCE_FAIL=1: every call returns QVAE_EFORCED before any launch
+    code = (
+        "import ctypes, sys\n"
+        "from w8a8_int8_quantized_act_amd import ops\n"
+        "L = ops.lib(); F = ctypes.c_void_p(0x10000)\n"
+        "r = [L.qvae_act_absmax(F, 16, F, None),\n"
+        "     L.qvae_act_quantize(F, 16, 1.0, F, F, F, None),\n"
+        "     L.qvae_act_absmax_quant(F, 16, 1.0, F, F, F, None),\n"
+        "     L.qvae_quantize_weights(F, 32, 32, 3, 3, 3, 1.0, F, F, None),\n"
+        "     L.qvae_causalconv3d_w8a8(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
+        "     L.qvae_causalconv3d_w8a8_acc32(F, None, F, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None)]\n"
+        "sys.exit(0 if r == [-4] * 6 else 1)\n")
+    env = dict(os.environ, QVAE_FORCE_FAIL="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_binding_raises_when_library_missing(monkeypatch):
+    from w8a8_int8_quantized_act_amd import ops
+    monkeypatch.setattr(ops, "_lib", None)
+    monkeypatch.setattr(ops, "LIB_PATH", "/nonexistent/libqvae.so")
+    with pytest.raises(ops.QvaeError):
+        ops.lib()
+
+
+def test_product_never_reaches_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
+                assert "qvae_oracle" not in src and "libqvae_oracle" not in src, f

@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: INT8 codes, scales (as bit patterns) and INT32 accumulators bit-exact;
+bf16 outputs within 1 bf16 ulp of the oracle's bf16 (ordinal distance of the
+bit patterns), which is the stated tolerance for the FP32-rescaled output.
+Small shapes are compared element by element over the whole output; the full
+workload sizes are compared on sampled output positions (corners, edges,
+tile seams, ragged tails, random) plus properties that hold at any size
+(chunked == unchunked, zero cache == front padding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from w8a8_int8_quantized_act_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w8a8_int8_quantized_act_amd import ops as o
+    o.lib()          # raises when the HIP library is missing
+    return o
+
+
+DEV = "cuda:0"
+
+
+def to_dev_bits(x_bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ulp_dist(a, b):
+    def ordv(h):
+        h = h.astype(np.int64)
+        return np.where(h & 0x8000, -(h & 0x7FFF), h)
+    return np.abs(ordv(a) - ordv(b))
+
+
+def f32_bits(v) -> int:
+    return int(np.float32(v).view(np.uint32))
+
+
+# ------------------------------------------------------------------ activation quantization
+def _check_act(ops, x_bits):
+    xd = to_dev_bits(x_bits)
+    absmax_bits, x_scale, xq = ops.act_absmax_quant(xd)
+    torch.cuda.synchronize()
+    a, s, q = oracle.act_absmax_quant(x_bits)
+    assert int(absmax_bits.item()) == f32_bits(a) >> 16
+    assert f32_bits(x_scale.item()) == f32_bits(s)
+    got = xq.cpu().numpy()
+    bad = np.count_nonzero(got != q)
+    assert bad == 0, f"{bad} of {q.size} codes differ"
+
+
+def _bits_of(x: torch.Tensor) -> np.ndarray:
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 15, 16, 17, 4097, 65536 * 3 + 5])
+def test_act_quant_sizes(ops, n):
+    g = torch.Generator().manual_seed(100 + n % 97)
+    _check_act(ops, _bits_of(torch.randn(n, generator=g) * 3))
+
+
+def test_act_quant_outliers_large(ops):
+    g = torch.Generator().manual_seed(101)
+    x = torch.randn(3_000_011, generator=g)
+    m = torch.rand(x.shape, generator=g) < 0.05
+    _check_act(ops, _bits_of(torch.where(m, x * 20, x)))
+
+
+def test_act_quant_ties_scale_one(ops):
+    # absmax 127 -> scale exactly 1: x.5 values are ties and go to the even code
+    vals = [127.0] + [k + 0.5 for k in range(-127, 127)] + [-127.0, 0.0, -0.0, 0.25, -0.75]
+    _check_act(ops, _bits_of(torch.tensor(vals * 37, dtype=torch.float32)))
+
+
+def test_act_quant_near_ties(ops):
+    # many values whose quotient lands within a few ulps of a half-integer
+    g = torch.Generator().manual_seed(102)
+    base = torch.randint(-126, 126, (200_000,), generator=g).float() + 0.5
+    a = torch.tensor([93.0])      # scale 93/127: quotients are near, not at, the ties
+    x = torch.cat([a, base * (93.0 / 127.0)])
+    _check_act(ops, _bits_of(x))
+
+
+def test_act_quant_zero_and_tiny(ops):
+    _check_act(ops, np.zeros(1000, np.uint16))
+    _check_act(ops, np.array([0x8000] * 33, np.uint16))           # -0.0 only
+    g = torch.Generator().manual_seed(103)
+    tiny = torch.randn(5000, generator=g) * 1e-39                 # bf16 subnormals: 1/s is not finite
+    _check_act(ops, _bits_of(tiny))
+    big = torch.randn(5000, generator=g) * 1e37
+    _check_act(ops, _bits_of(big))
+
+
+# ------------------------------------------------------------------ weight quantization
+@pytest.mark.parametrize("shape", [(384, 384, 3, 3, 3), (192, 384, 1, 1, 1), (96, 96, 3, 3, 3), (32, 64, 3, 1, 1)])
+def test_weight_quant_bitexact(ops, shape):
+    g = torch.Generator().manual_seed(200 + shape[0])
+    w = torch.randn(shape, generator=g) * 0.02
+    w[1] = 0.0                                   # an all-zero channel
+    w[2].view(-1)[5] = 0.5                       # a channel with one large weight
+    wq, ws = ops.quantize_weights(w.to(DEV))
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_weights(w.numpy())
+    assert np.array_equal(ws.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(wq.cpu().numpy(), rq)
+
+
+# ------------------------------------------------------------------ the convolution, small shapes
+SMALL = [
+    # N, T, H, W, Cin, Cout, k, cache
+    (1, 4, 32, 32, 96, 96, (3, 3, 3), False),
+    (2, 3, 19, 37, 64, 192, (3, 3, 3), False),
+    (1, 2, 17, 33, 64, 384, (3, 3, 3), True),
+    (1, 1, 9, 40, 32, 96, (3, 3, 3), True),
+    (2, 2, 11, 13, 96, 64, (3, 3, 3), False),
+    (1, 3, 5, 7, 32, 32, (3, 3, 3), True),
+    (1, 1, 1, 1, 32, 32, (3, 3, 3), False),
+    (1, 2, 20, 31, 384, 192, (1, 1, 1), False),
+    (1, 3, 8, 24, 64, 96, (3, 1, 1), True),
+    (1, 1, 25, 18, 192, 192, (1, 3, 3), False),
+]
+
+
+def _small_inputs(case, seed):
+    N, T, H, W, Cin, Cout, k, with_cache = case
+    ci = wl.draw_custom(seed, N, Cin, Cout, T, H, W, k=k)
+    wq, ws = oracle.quantize_weights(ci.w)
+    a, s, xq = oracle.act_absmax_quant(ci.x)
+    cache = None
+    if with_cache and k[0] > 1:
+        g = torch.Generator().manual_seed(seed + 1)
+        cache = torch.randint(-127, 128, (N, k[0] - 1, H, W, Cin), generator=g,
+                              dtype=torch.int64).numpy().astype(np.int8)
+    return ci, wq, ws, s, xq, cache
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[0]}x{c[1]}x{c[2]}x{c[3]}_c{c[4]}-{c[5]}_k{''.join(map(str, c[6]))}"
+                                             f"{'_cache' if c[7] else ''}" for c in SMALL])
+def test_conv_small_full(ops, case):
+    ci, wq, ws, s, xq, cache = _small_inputs(case, 300 + sum(case[:6]))
+    ref_acc = oracle.conv_acc(xq, wq, cache)
+    ref_y = oracle.epilogue(ref_acc, s, ws, ci.b)
+
+    xq_d = torch.from_numpy(xq).to(DEV)
+    wq_d = torch.from_numpy(wq).to(DEV)
+    cache_d = None if cache is None else torch.from_numpy(cache).to(DEV)
+    acc = ops.causalconv3d_w8a8_acc32(xq_d, wq_d, cache_d)
+    y = ops.causalconv3d_w8a8(xq_d, torch.tensor([s], device=DEV), wq_d, torch.from_numpy(ws).to(DEV),
+                              torch.from_numpy(ci.b).to(DEV), cache_d)
+    torch.cuda.synchronize()
+    got_acc = acc.cpu().numpy()
+    bad = np.argwhere(got_acc != ref_acc)
+    assert bad.shape[0] == 0, f"{bad.shape[0]} accumulators differ, first at {bad[:4].tolist()}"
+    d = ulp_dist(bf16_bits(y), ref_y)
+    assert d.max() <= 1
+    assert np.count_nonzero(d) == 0, f"{np.count_nonzero(d)} bf16 outputs differ by 1 ulp"
+
+
+def test_conv_no_bias(ops):
+    ci, wq, ws, s, xq, cache = _small_inputs((1, 2, 9, 21, 64, 96, (3, 3, 3), False), 350)
+    ref_y = oracle.epilogue(oracle.conv_acc(xq, wq), s, ws, None)
+    y = ops.causalconv3d_w8a8(torch.from_numpy(xq).to(DEV), torch.tensor([s], device=DEV),
+                              torch.from_numpy(wq).to(DEV), torch.from_numpy(ws).to(DEV), None)
+    torch.cuda.synchronize()
+    assert ulp_dist(bf16_bits(y), ref_y).max() == 0
+
+
+def test_layer_end_to_end_small(ops):
+    # bf16 x -> (GPU absmax, quantize, weight quant, conv) vs the oracle's layer
+    ci = wl.draw_custom(360, 1, 96, 96, 3, 23, 29, x_kind="silu")
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    y, xs, xq = ops.layer_forward(to_dev_bits(ci.x), wq_d, ws_d, torch.from_numpy(ci.b).to(DEV))
+    torch.cuda.synchronize()
+    wq, ws = oracle.quantize_weights(ci.w)
+    ref_y, ref_s = oracle.layer(ci.x, wq, ws, ci.b)
+    assert f32_bits(xs.item()) == f32_bits(ref_s)
+    assert ulp_dist(bf16_bits(y), ref_y).max() == 0
+
+
+# ------------------------------------------------------------------ full workload sizes
+def sample_positions(N, T, H, W, n_random, seed):
+    """Flattened (n, t, h, w) positions: corners, image edges, tile seams of
+    8/16/32-pixel tiles, the ragged last row/column, and random ones."""
+    rng = np.random.default_rng(seed)
+    hs = sorted(set([0, 1, H - 2, H - 1] + [v for m in (8, 16) for k in range(m, H, m * 5) for v in (k - 1, k)]))
+    ws = sorted(set([0, 1, W - 2, W - 1] + [v for m in (16, 32) for k in range(m, W, m * 5) for v in (k - 1, k)]))
+    hs = [h for h in hs if 0 <= h < H]
+    ws = [w for w in ws if 0 <= w < W]
+    pos = []
+    for n in range(N):
+        for t in sorted(set([0, T - 1, min(1, T - 1), min(2, T - 1)])):
+            for h in hs:
+                for w in (ws[:3] + ws[-3:]):
+                    pos.append(((n * T + t) * H + h) * W + w)
+            for w in ws:
+                for h in (hs[:2] + hs[-2:]):
+                    pos.append(((n * T + t) * H + h) * W + w)
+    pos += list(rng.integers(0, N * T * H * W, n_random))
+    return np.unique(np.array(pos, np.int64))
+
+
+def _run_full_conv(ops, ci, cache_zero=False):
+    spec = ci.spec
+    kt = spec.k[0]
+    x_d = to_dev_bits(ci.x)
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    b_d = torch.from_numpy(ci.b).to(DEV)
+    absmax, xs, xq_d = ops.act_absmax_quant(x_d)
+    cache_d = None
+    if cache_zero:
+        cache_d = torch.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), dtype=torch.int8, device=DEV)
+    y = ops.causalconv3d_w8a8(xq_d, xs, wq_d, ws_d, b_d, cache_d)
+    acc = ops.causalconv3d_w8a8_acc32(xq_d, wq_d, cache_d)
+    torch.cuda.synchronize()
+    return dict(x_d=x_d, wq_d=wq_d, ws_d=ws_d, b_d=b_d, absmax=absmax, xs=xs, xq_d=xq_d, y=y, acc=acc,
+                cache_d=cache_d)
+
+
+def _compare_full(ops, ci, r, n_random=1500, seed=0, cache_zero=False):
+    spec = ci.spec
+    wq, ws = oracle.quantize_weights(ci.w)
+    assert np.array_equal(r["wq_d"].cpu().numpy(), wq)
+    assert np.array_equal(r["ws_d"].cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    a, s, xq = oracle.act_absmax_quant(ci.x)
+    assert int(r["absmax"].item()) == f32_bits(a) >> 16
+    assert f32_bits(r["xs"].item()) == f32_bits(s)
+    got_xq = r["xq_d"].cpu().numpy()
+    assert np.array_equal(got_xq, xq), f"{np.count_nonzero(got_xq != xq)} codes differ"
+    # nothing is clamped at clip ratio 1.0: the largest code is exactly 127 in magnitude
+    assert np.abs(xq.astype(np.int16)).max() == 127
+    pos = sample_positions(spec.N, spec.T, spec.H, spec.W, n_random, seed)
+    cache = np.zeros((spec.N, spec.k[0] - 1, spec.H, spec.W, spec.Cin), np.int8) if cache_zero else None
+    ref_acc = oracle.conv_acc(xq, wq, cache, positions=pos)
+    ref_y = oracle.epilogue(ref_acc, s, ws, ci.b)
+    got_acc = r["acc"].reshape(-1, spec.Cout)[torch.from_numpy(pos).to(DEV)].cpu().numpy()
+    got_y = bf16_bits(r["y"].reshape(-1, spec.Cout)[torch.from_numpy(pos).to(DEV)])
+    assert np.array_equal(got_acc, ref_acc), f"{np.count_nonzero(got_acc != ref_acc)} accumulators differ"
+    d = ulp_dist(got_y, ref_y)
+    assert d.max() <= 1 and np.count_nonzero(d) == 0
+    # the bf16 output and the INT32 export agree everywhere (same contraction, same epilogue)
+    return pos
+
+
+def test_workload_single_96_t4_32_full(ops):
+    ci = wl.draw_workload("single_96_t4_32")[0]
+    r = _run_full_conv(ops, ci)
+    wq, ws = oracle.quantize_weights(ci.w)
+    y_ref, s = oracle.layer(ci.x, wq, ws, ci.b)
+    assert f32_bits(r["xs"].item()) == f32_bits(s)
+    assert ulp_dist(bf16_bits(r["y"]), y_ref).max() == 0
+    a, s, xq = oracle.act_absmax_quant(ci.x)
+    assert np.array_equal(r["acc"].cpu().numpy(), oracle.conv_acc(xq, wq))
+
+
+def test_workload_latent_384_128_cache(ops):
+    ci = wl.draw_workload("latent_384_128_cache")[0]
+    r = _run_full_conv(ops, ci, cache_zero=True)
+    _compare_full(ops, ci, r, seed=1, cache_zero=True)
+    # a zero cache equals causal front padding, bit for bit, at full size
+    y2 = ops.causalconv3d_w8a8(r["xq_d"], r["xs"], r["wq_d"], r["ws_d"], r["b_d"], None)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), r["y"].view(torch.int16))
+
+
+@pytest.mark.parametrize("level", [0, 1, 2, 3])
+def test_workload_sweep_1024(ops, level):
+    ci = wl.draw_workload("sweep_1024", only=level)[0]
+    r = _run_full_conv(ops, ci)
+    _compare_full(ops, ci, r, seed=20 + level)
+
+
+@pytest.mark.parametrize("level", [0, 1, 2, 3])
+def test_workload_sweep_840x1256(ops, level):
+    ci = wl.draw_workload("sweep_840x1256", only=level)[0]
+    r = _run_full_conv(ops, ci)
+    _compare_full(ops, ci, r, seed=30 + level)
+
+
+def test_workload_video_chunked(ops):
+    ci = wl.draw_workload("video_384_t8_chunked")[0]
+    spec = ci.spec
+    x_d = to_dev_bits(ci.x)
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    b_d = torch.from_numpy(ci.b).to(DEV)
+    wp_d, wps_d = ops.quantize_weights(torch.from_numpy(ci.w_proj).to(DEV))
+    bp_d = torch.from_numpy(ci.b_proj).to(DEV)
+    _, xs, xq_d = ops.act_absmax_quant(x_d)        # one scale over all 8 frames
+    full = ops.causalconv3d_w8a8(xq_d, xs, wq_d, ws_d, b_d)
+    chunked = torch.empty_like(full)
+    fpc = spec.T // spec.chunks
+    for c in range(spec.chunks):
+        cache = None if c == 0 else xq_d[:, fpc * c - 2:fpc * c]
+        ops.causalconv3d_w8a8(xq_d[:, fpc * c:fpc * (c + 1)], xs, wq_d, ws_d, b_d, cache,
+                              out=chunked[:, fpc * c:fpc * (c + 1)])
+    proj = ops.causalconv3d_w8a8(xq_d, xs, wp_d, wps_d, bp_d)
+    acc = ops.causalconv3d_w8a8_acc32(xq_d, wq_d)
+    torch.cuda.synchronize()
+    # chunked decode equals the single pass, bit for bit
+    assert torch.equal(full.view(torch.int16), chunked.view(torch.int16))
+    # both against the oracle on sampled positions
+    wq, ws = oracle.quantize_weights(ci.w)
+    wp, wps = oracle.quantize_weights(ci.w_proj)
+    a, s, xq = oracle.act_absmax_quant(ci.x)
+    assert np.array_equal(xq_d.cpu().numpy(), xq)
+    pos = sample_positions(spec.N, spec.T, spec.H, spec.W, 1500, 4)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    ref_acc = oracle.conv_acc(xq, wq, None, positions=pos)
+    assert np.array_equal(acc.reshape(-1, spec.Cout)[pos_d].cpu().numpy(), ref_acc)
+    ref_y = oracle.epilogue(ref_acc, s, ws, ci.b)
+    assert ulp_dist(bf16_bits(chunked.reshape(-1, spec.Cout)[pos_d]), ref_y).max() == 0
+    ref_p = oracle.epilogue(oracle.conv_acc(xq, wp, None, positions=pos), s, wps, ci.b_proj)
+    assert ulp_dist(bf16_bits(proj.reshape(-1, spec.proj_cout)[pos_d]), ref_p).max() == 0

@@ -1,0 +1,222 @@
+// qvae_act.hip -- dynamic per-tensor INT8 activation quantization on gfx950.
+//
+// Scheme (page "ComfyUI-Qwen-VAE-Triton v0.2.0", section "Three presets
+// explained"): activations are dynamically, symmetrically quantized to INT8
+// with clip ratio 1.0.  One scale per tensor: s = fl(absmax) / 127 and
+// q = clamp(rne(x / s), -127, 127).
+//
+// Two HBM-bound passes.  The scale is a grid-wide dependency, so the max is
+// reduced first (pass 1) and every quantize workgroup derives the same scale
+// from the reduced word (pass 2); the scale never visits the host.
+//
+//   pass 1  k_absmax    16-byte loads of bf16, integer max of |x| bit patterns
+//                       (for finite bf16, |a| < |b| iff (a & 0x7FFF) <
+//                       (b & 0x7FFF) as integers), packed 2x16-bit max, DPP
+//                       wave reduction, LDS workgroup reduction, one atomicMax
+//                       per workgroup into the output word (cleared first by a
+//                       one-lane kernel on the same stream).
+//   pass 2  k_quantize  32 bytes of bf16 in, 16 int8 codes out per lane.
+//
+// The quotient x / s is the IEEE binary32 one.  The kernel computes t = x * r
+// with r = fl(1 / s) and keeps rne(t) when t is far from a rounding boundary:
+// |fl(x*r) - x/s| <= |x/s| * (2^-23 + 2^-46) and |fl(x/s) - x/s| <= |x/s| * 2^-24,
+// so when t is more than |t| * 2^-20 away from every half-integer, t and
+// fl(x/s) round to the same integer.  Otherwise (and whenever 1/s is not
+// finite) it performs the correctly rounded division itself.
+#include "qvae_internal.h"
+
+namespace qvae {
+
+typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(64) void k_absmax_clear(uint32_t *word) { *word = 0u; }
+
+// Packed 2x16-bit unsigned max of the magnitudes held in one 32-bit word.
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
+{
+    ushort2_t a = __builtin_bit_cast(ushort2_t, acc);
+    ushort2_t b = __builtin_bit_cast(ushort2_t, w & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+constexpr int kAbsmaxThreads = 256;
+constexpr int kAbsmaxUnroll = 4;   // 16-byte loads in flight per lane
+
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restrict__ x16,
+                                                          int64_t n16,
+                                                          const uint16_t *__restrict__ tail,
+                                                          int ntail,
+                                                          uint32_t *__restrict__ out)
+{
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * kAbsmaxThreads;
+    int64_t i = (int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x;
+    for (; i + (kAbsmaxUnroll - 1) * stride < n16; i += kAbsmaxUnroll * stride) {
+        u32x4 v[kAbsmaxUnroll];
+#pragma unroll
+        for (int u = 0; u < kAbsmaxUnroll; ++u) v[u] = __builtin_nontemporal_load(&x16[i + u * stride]);
+#pragma unroll
+        for (int u = 0; u < kAbsmaxUnroll; ++u) {
+            m = pk_absmax(m, v[u].x);
+            m = pk_absmax(m, v[u].y);
+            m = pk_absmax(m, v[u].z);
+            m = pk_absmax(m, v[u].w);
+        }
+    }
+    for (; i < n16; i += stride) {
+        u32x4 v = x16[i];
+        m = pk_absmax(m, v.x);
+        m = pk_absmax(m, v.y);
+        m = pk_absmax(m, v.z);
+        m = pk_absmax(m, v.w);
+    }
+    if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = pk_absmax(m, tail[threadIdx.x]);
+    m = max(m & 0xFFFFu, m >> 16);
+    m = wave_max_u32(m);
+
+    __shared__ uint32_t part[kAbsmaxThreads / 64];
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) part[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = part[0];
+#pragma unroll
+        for (int k = 1; k < kAbsmaxThreads / 64; ++k) b = max(b, part[k]);
+        atomicMax(out, b);
+    }
+}
+
+// One activation code: clamp(rne(x / s), -127, 127).
+__device__ __forceinline__ int quant_code(float x, float s, float r, bool exact_only)
+{
+    float t = x * r;
+    float n = __builtin_rintf(t);
+    float dist = fabsf(fabsf(t - n) - 0.5f);       // distance to the nearest half-integer
+    if (exact_only || !(dist > fabsf(t) * 0x1p-20f)) {
+        t = x / s;                                   // correctly rounded division
+        n = __builtin_rintf(t);
+    }
+    n = fminf(fmaxf(n, -127.0f), 127.0f);
+    return (int)n;
+}
+
+__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s, float r, bool ex)
+{
+    // lo, hi: two words of two bf16 each -> four int8 codes in one word
+    int q0 = quant_code(bf16_bits_to_float(lo & 0xFFFFu), s, r, ex);
+    int q1 = quant_code(bf16_bits_to_float(lo >> 16), s, r, ex);
+    int q2 = quant_code(bf16_bits_to_float(hi & 0xFFFFu), s, r, ex);
+    int q3 = quant_code(bf16_bits_to_float(hi >> 16), s, r, ex);
+    return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+           ((uint32_t)(q3 & 0xFF) << 24);
+}
+
+constexpr int kQuantThreads = 256;
+
+// Each lane: 16 bf16 (two 16-byte loads) -> 16 codes (one 16-byte store).
+__global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restrict__ x16,
+                                                           int64_t n32,   // groups of 16 elements
+                                                           const uint16_t *__restrict__ x,
+                                                           int64_t numel,
+                                                           float clip_ratio,
+                                                           const uint32_t *__restrict__ absmax_bits,
+                                                           float *__restrict__ x_scale,
+                                                           u32x4 *__restrict__ q16,
+                                                           int8_t *__restrict__ q)
+{
+    const float a = bf16_bits_to_float(*absmax_bits);
+    const float s = (clip_ratio * a) / 127.0f;
+    const float r = 1.0f / s;
+    const bool zero = !(s > 0.0f);
+    const bool exact_only = !(r < __builtin_inff());
+    if (blockIdx.x == 0 && threadIdx.x == 0) *x_scale = s;
+
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n32; i += stride) {
+        u32x4 v0 = __builtin_nontemporal_load(&x16[2 * i]);
+        u32x4 v1 = __builtin_nontemporal_load(&x16[2 * i + 1]);
+        u32x4 o;
+        if (zero) {
+            o = u32x4{0u, 0u, 0u, 0u};
+        } else {
+            o.x = quant4(v0.x, v0.y, s, r, exact_only);
+            o.y = quant4(v0.z, v0.w, s, r, exact_only);
+            o.z = quant4(v1.x, v1.y, s, r, exact_only);
+            o.w = quant4(v1.z, v1.w, s, r, exact_only);
+        }
+        q16[i] = o;
+    }
+    // the last numel % 16 elements, one per lane of workgroup 0
+    if (blockIdx.x == 0) {
+        int64_t e = n32 * 16 + threadIdx.x;
+        if (e < numel) {
+            q[e] = zero ? 0 : (int8_t)quant_code(bf16_bits_to_float(x[e]), s, r, exact_only);
+        }
+    }
+}
+
+static int device_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
+}  // namespace qvae
+
+using namespace qvae;
+
+extern "C" int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax_bits, void *stream)
+{
+    if (force_fail()) return QVAE_EFORCED;
+    if (!x || !absmax_bits || numel <= 0) return QVAE_EINVAL;
+    if (!aligned16(x)) return QVAE_EINVAL;
+    hipStream_t st = as_stream(stream);
+    const int64_t n16 = numel / 8;
+    const int ntail = (int)(numel - n16 * 8);
+    int64_t want = (n16 + (int64_t)kAbsmaxThreads * kAbsmaxUnroll - 1) / ((int64_t)kAbsmaxThreads * kAbsmaxUnroll);
+    int64_t cap = (int64_t)device_cus() * 8;
+    int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+    hipLaunchKernelGGL(k_absmax_clear, dim3(1), dim3(64), 0, st, absmax_bits);
+    hipLaunchKernelGGL(k_absmax, dim3(blocks), dim3(kAbsmaxThreads), 0, st,
+                       reinterpret_cast<const u32x4 *>(x), n16, x + n16 * 8, ntail, absmax_bits);
+    return launch_status();
+}
+
+extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
+                                 const uint32_t *absmax_bits, float *x_scale, int8_t *xq, void *stream)
+{
+    if (force_fail()) return QVAE_EFORCED;
+    if (!x || !absmax_bits || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
+    if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
+    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    hipStream_t st = as_stream(stream);
+    const int64_t n32 = numel / 16;
+    int64_t want = (n32 + kQuantThreads - 1) / kQuantThreads;
+    int64_t cap = (int64_t)device_cus() * 16;
+    int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+    hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, st,
+                       reinterpret_cast<const u32x4 *>(x), n32, x, numel, clip_ratio, absmax_bits,
+                       x_scale, reinterpret_cast<u32x4 *>(xq), xq);
+    return launch_status();
+}
+
+extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
+                                     uint32_t *absmax_bits, float *x_scale, int8_t *xq, void *stream)
+{
+    if (force_fail()) return QVAE_EFORCED;
+    if (!x || !absmax_bits || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
+    if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
+    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    int rc = qvae_act_absmax(x, numel, absmax_bits, stream);
+    if (rc != QVAE_OK) return rc;
+    return qvae_act_quantize(x, numel, clip_ratio, absmax_bits, x_scale, xq, stream);
+}

@@ -1,0 +1,63 @@
+// qvae_internal.h -- helpers shared by the HIP sources of libqvae (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "qvae.h"
+
+namespace qvae {
+
+// Every entry point starts with this: the fallback test hook, then nothing.
+inline bool force_fail()
+{
+    const char *v = getenv("QVAE_FORCE_FAIL");
+    return v && v[0] == '1';
+}
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Map the state after a launch to a status code (never throws or aborts).
+inline int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? QVAE_OK : QVAE_ELAUNCH;
+}
+
+// ---- device helpers -------------------------------------------------------
+
+// bf16 bit pattern -> float (exact widening).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h)
+{
+    return __uint_as_float(h << 16);
+}
+
+// float -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Maximum of an unsigned value over the 64 lanes of a wavefront: DPP
+// exchanges inside each row of 16 lanes, then the four row results are read
+// with readlane.  Every lane returns the wave maximum.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+}  // namespace qvae

@@ -1,0 +1,92 @@
+// qvae_wquant.hip -- per-output-channel symmetric INT8 weight quantization.
+//
+// Scheme (page "ComfyUI-Qwen-VAE-Triton v0.2.0", section "Three presets
+// explained"): symmetric INT8 weights, one scale per output channel, weight
+// clip ratio 1.0.  s[co] = fl(max |w[co,...]|) / 127 over every
+// (ci, kt, kh, kw) of the channel; q = clamp(rne(w / s[co]), -127, 127).
+//
+// Runs once per layer at load time.  One workgroup per output channel: a
+// max-reduction over the channel (non-negative floats compare like their bit
+// patterns, so the DPP integer max applies), then every lane quantizes and
+// scatters into the K-contiguous layout [Cout][kt][kh][kw][Cin] the
+// convolution reads.
+#include "qvae_internal.h"
+
+namespace qvae {
+
+constexpr int kWqThreads = 256;
+
+__global__ __launch_bounds__(kWqThreads) void k_quantize_weights(const float *__restrict__ w, int Cin,
+                                                                 int kt, int kh, int kw,
+                                                                 float clip_ratio,
+                                                                 int8_t *__restrict__ wq,
+                                                                 float *__restrict__ w_scale)
+{
+    const int co = blockIdx.x;
+    const int taps = kt * kh * kw;
+    const int64_t per_co = (int64_t)Cin * taps;
+    const float *wc = w + (int64_t)co * per_co;
+
+    uint32_t m = 0;
+    for (int64_t e = threadIdx.x; e < per_co; e += kWqThreads) m = max(m, __float_as_uint(fabsf(wc[e])));
+    m = wave_max_u32(m);
+    __shared__ uint32_t part[kWqThreads / 64];
+    __shared__ float s_sh;
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t b = part[0];
+#pragma unroll
+        for (int k = 1; k < kWqThreads / 64; ++k) b = max(b, part[k]);
+        float s = (clip_ratio * __uint_as_float(b)) / 127.0f;
+        s_sh = s;
+        w_scale[co] = s;
+    }
+    __syncthreads();
+    const float s = s_sh;
+
+    // source order [ci][tap] (tap = (i*kh + j)*kw + l); destination [tap][ci]
+    int8_t *dst = wq + (int64_t)co * per_co;
+    for (int64_t e = threadIdx.x; e < per_co; e += kWqThreads) {
+        const int ci = (int)(e / taps);
+        const int tap = (int)(e - (int64_t)ci * taps);
+        int q = 0;
+        if (s > 0.0f) {
+            float t = wc[e] / s;   // correctly rounded division
+            t = fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
+            q = (int)t;
+        }
+        dst[(int64_t)tap * Cin + ci] = (int8_t)q;
+    }
+}
+
+}  // namespace qvae
+
+using namespace qvae;
+
+extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh, int kw,
+                                     float clip_ratio, int8_t *wq, float *w_scale, void *stream)
+{
+    if (force_fail()) return QVAE_EFORCED;
+    if (!w || !wq || !w_scale || Cout <= 0 || Cin <= 0 || kt <= 0 || kh <= 0 || kw <= 0)
+        return QVAE_EINVAL;
+    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    if ((kt != 1 && kt != 3) || (kh != 1 && kh != 3) || (kw != 1 && kw != 3)) return QVAE_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_quantize_weights, dim3(Cout), dim3(kWqThreads), 0, as_stream(stream), w, Cin,
+                       kt, kh, kw, clip_ratio, wq, w_scale);
+    return launch_status();
+}
+
+extern "C" int qvae_version(void) { return (0 << 16) | 1; }
+
+extern "C" const char *qvae_strerror(int status)
+{
+    switch (status) {
+    case QVAE_OK: return "ok";
+    case QVAE_EINVAL: return "invalid argument (null pointer, non-positive size or misaligned buffer)";
+    case QVAE_EUNSUPPORTED: return "unsupported configuration";
+    case QVAE_ELAUNCH: return "kernel launch failed";
+    case QVAE_EFORCED: return "failure forced by QVAE_FORCE_FAIL";
+    default: return "unknown status";
+    }
+}

@@ -1,0 +1,210 @@
+"""Thin Python binding of libqvae (ctypes): argument marshalling only.
+
+Every step of the path runs in the HIP kernels behind the C ABI declared in
+``include/qvae.h``; this module only turns torch tensors into device pointers
+and the current torch stream into a ``hipStream_t``.  Torch provides device
+memory and streams.  There is no fallback here: a missing library or a
+non-zero status raises ``QvaeError`` (the caller decides what to do, e.g. run
+its native-precision layer instead).
+
+Names follow the C entry points:
+  quantize_weights        -> qvae_quantize_weights
+  act_absmax              -> qvae_act_absmax
+  act_quantize            -> qvae_act_quantize
+  act_absmax_quant        -> qvae_act_absmax_quant
+  causalconv3d_w8a8       -> qvae_causalconv3d_w8a8
+  causalconv3d_w8a8_acc32 -> qvae_causalconv3d_w8a8_acc32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqvae.so")
+
+OK, EINVAL, EUNSUPPORTED, ELAUNCH, EFORCED = 0, -1, -2, -3, -4
+
+
+class QvaeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = strerror(status) if _lib is not None else ""
+        super().__init__(f"{where}: {text} (status {status})" if text else f"{where} (status {status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqvae.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QvaeError(ELAUNCH, f"HIP library not built: {LIB_PATH} is missing "
+                                     "(run python -m w8a8_int8_quantized_act_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+        L.qvae_version.argtypes = []
+        L.qvae_version.restype = i32
+        L.qvae_strerror.argtypes = [i32]
+        L.qvae_strerror.restype = ctypes.c_char_p
+        L.qvae_quantize_weights.argtypes = [P, i32, i32, i32, i32, i32, f32, P, P, P]
+        L.qvae_quantize_weights.restype = i32
+        L.qvae_act_absmax.argtypes = [P, i64, P, P]
+        L.qvae_act_absmax.restype = i32
+        L.qvae_act_quantize.argtypes = [P, i64, f32, P, P, P, P]
+        L.qvae_act_quantize.restype = i32
+        L.qvae_act_absmax_quant.argtypes = [P, i64, f32, P, P, P, P]
+        L.qvae_act_absmax_quant.restype = i32
+        L.qvae_causalconv3d_w8a8.argtypes = [P, P, P, P, P, P] + [i32] * 9 + [P, P]
+        L.qvae_causalconv3d_w8a8.restype = i32
+        L.qvae_causalconv3d_w8a8_acc32.argtypes = [P, P, P] + [i32] * 9 + [P, P]
+        L.qvae_causalconv3d_w8a8_acc32.restype = i32
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qvae_strerror(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise QvaeError(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ------------------------------------------------------------------ weights
+def quantize_weights(w: torch.Tensor, clip_ratio: float = 1.0, stream=None):
+    """w float32 [Cout][Cin][kt][kh][kw] -> (wq int8 [Cout][kt][kh][kw][Cin], w_scale float32 [Cout])."""
+    _dev(w, "w", torch.float32)
+    Cout, Cin, kt, kh, kw = w.shape
+    wq = torch.empty((Cout, kt, kh, kw, Cin), dtype=torch.int8, device=w.device)
+    ws = torch.empty((Cout,), dtype=torch.float32, device=w.device)
+    _check(lib().qvae_quantize_weights(_p(w), Cout, Cin, kt, kh, kw, float(clip_ratio),
+                                       _p(wq), _p(ws), _stream(stream)), "qvae_quantize_weights")
+    return wq, ws
+
+
+# ------------------------------------------------------------------ activations
+def _bits_view(x: torch.Tensor):
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError(f"x must hold bf16 values, got {x.dtype}")
+    return x
+
+
+def act_absmax(x: torch.Tensor, absmax_bits: torch.Tensor | None = None, stream=None):
+    """-> int32 [1] device tensor holding the bf16 bit pattern of max |x|."""
+    _dev(_bits_view(x), "x")
+    if absmax_bits is None:
+        absmax_bits = torch.empty((1,), dtype=torch.int32, device=x.device)
+    _check(lib().qvae_act_absmax(_p(x), x.numel(), _p(absmax_bits), _stream(stream)), "qvae_act_absmax")
+    return absmax_bits
+
+
+def act_quantize(x: torch.Tensor, absmax_bits: torch.Tensor, clip_ratio: float = 1.0,
+                 x_scale: torch.Tensor | None = None, xq: torch.Tensor | None = None, stream=None):
+    """-> (x_scale float32 [1], xq int8 of x's shape)."""
+    _dev(_bits_view(x), "x")
+    if x_scale is None:
+        x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    if xq is None:
+        xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _check(lib().qvae_act_quantize(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
+                                   _p(xq), _stream(stream)), "qvae_act_quantize")
+    return x_scale, xq
+
+
+def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None, x_scale=None, xq=None,
+                     stream=None):
+    """-> (absmax_bits int32 [1], x_scale float32 [1], xq int8 of x's shape)."""
+    _dev(_bits_view(x), "x")
+    dev = x.device
+    if absmax_bits is None:
+        absmax_bits = torch.empty((1,), dtype=torch.int32, device=dev)
+    if x_scale is None:
+        x_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    if xq is None:
+        xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    _check(lib().qvae_act_absmax_quant(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
+                                       _p(xq), _stream(stream)), "qvae_act_absmax_quant")
+    return absmax_bits, x_scale, xq
+
+
+# ------------------------------------------------------------------ convolution
+def _conv_dims(xq, wq, cache):
+    _dev(xq, "xq", torch.int8)
+    _dev(wq, "wq", torch.int8)
+    N, T, H, W, Cin = xq.shape
+    Cout, kt, kh, kw, Cin2 = wq.shape
+    if Cin2 != Cin:
+        raise ValueError(f"Cin mismatch: xq has {Cin}, wq has {Cin2}")
+    if cache is not None:
+        _dev(cache, "cache", torch.int8)
+        if tuple(cache.shape) != (N, kt - 1, H, W, Cin):
+            raise ValueError(f"cache must be [N][kt-1][H][W][Cin] = {(N, kt - 1, H, W, Cin)}, "
+                             f"got {tuple(cache.shape)}")
+    return N, T, H, W, Cin, Cout, kt, kh, kw
+
+
+def causalconv3d_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                      bias: torch.Tensor | None = None, cache: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None, stream=None):
+    """xq int8 [N][T][H][W][Cin] -> y bf16 [N][T][H][W][Cout]."""
+    N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(w_scale, "w_scale", torch.float32)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+    if out is None:
+        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=xq.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (N, T, H, W, Cout):
+            raise ValueError("out shape")
+    _check(lib().qvae_causalconv3d_w8a8(_p(xq), _p(x_scale), _p(cache), _p(wq), _p(w_scale), _p(bias),
+                                        N, T, H, W, Cin, Cout, kt, kh, kw, _p(out), _stream(stream)),
+           "qvae_causalconv3d_w8a8")
+    return out
+
+
+def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Tensor | None = None,
+                            out: torch.Tensor | None = None, stream=None):
+    """Raw INT32 accumulators [N][T][H][W][Cout] (verification export)."""
+    N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
+    if out is None:
+        out = torch.empty((N, T, H, W, Cout), dtype=torch.int32, device=xq.device)
+    _check(lib().qvae_causalconv3d_w8a8_acc32(_p(xq), _p(cache), _p(wq), N, T, H, W, Cin, Cout, kt, kh, kw,
+                                              _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_acc32")
+    return out
+
+
+def layer_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
+                  cache: torch.Tensor | None = None, stream=None):
+    """One W8A8 CausalConv3d layer: absmax -> quantize -> implicit-GEMM conv.
+
+    x bf16 [N][T][H][W][Cin] -> (y bf16 [N][T][H][W][Cout], x_scale, xq)."""
+    _, x_scale, xq = act_absmax_quant(x, stream=stream)
+    y = causalconv3d_w8a8(xq, x_scale, wq, w_scale, bias, cache, stream=stream)
+    return y, x_scale, xq
