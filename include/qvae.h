@@ -27,7 +27,7 @@
  *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronize with the host;
  *   - layouts are channels-last: activations [N][T][H][W][C], contiguous;
- *   - x, xq, y, acc and cache must be 16-byte aligned;
+ *   - x, xq, wq, y, acc and cache must be 16-byte aligned;
  *   - the return value is a status code (QVAE_OK = 0, negative on error);
  *     arguments are validated before anything is launched; the library never
  *     aborts or throws; on a non-zero status the caller is expected to fall
@@ -64,12 +64,18 @@ const char *qvae_strerror(int status);
  * symmetric INT8 weights, one scale per output channel; fixed parameters:
  * weight clip ratio 1.0).
  *   w        float32 [Cout][Cin][kt][kh][kw]  (the usual Conv3d weight layout)
- *   wq       int8    [Cout][kt][kh][kw][Cin]  out (K-contiguous per channel)
+ *   wq       int8, Cout*Cin*kt*kh*kw bytes, out, 16-byte aligned, packed in
+ *            the order the convolution's matrix-core loop consumes it:
+ *              wq[cb][i][s][j*kw + l][L][b] = q(co = 32*cb + L%32, i, j, l,
+ *                                              ci = 32*s + 16*(L/32) + b)
+ *            for cb < Cout/32, s < Cin/32, L < 64, b < 16 (each [L][b] block
+ *            is one 1 KB operand fragment of 32 output x 32 input channels)
  *   w_scale  float32 [Cout]                   out
  * w_scale[co] = fl(clip * max |w[co,...]|) / 127, the maximum taken over
- * every (ci, kt, kh, kw); wq = clamp(rne(w / w_scale[co]), -127, 127), 0 for
+ * every (ci, kt, kh, kw); q = clamp(rne(w / w_scale[co]), -127, 127), 0 for
  * an all-zero channel.
- * Supported: clip_ratio == 1.0f, Cout, Cin >= 1, kt, kh, kw in {1, 3}.
+ * Supported: clip_ratio == 1.0f, Cout % 32 == 0, Cin % 32 == 0,
+ * kt, kh, kw in {1, 3}.
  */
 int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh,
                           int kw, float clip_ratio, int8_t *wq,
@@ -109,12 +115,12 @@ int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
  *   x_scale  float32 [1] (device; from qvae_act_quantize)
  *   cache    int8 [N][kt-1][H][W][Cin], the kt-1 frames before frame 0, oldest
  *            first, quantized with the same x_scale; NULL = zero front frames
- *   wq, w_scale  from qvae_quantize_weights
+ *   wq, w_scale  from qvae_quantize_weights (wq in its packed layout)
  *   bias     float32 [Cout] or NULL (zero)
  *   y        bf16 bit patterns [N][T][H][W][Cout] out
  * y[n,t,h,w,co] = bf16_rne(fma(float(acc), fl(x_scale * w_scale[co]),
  * bias[co])) with acc = sum over (i, j, l, ci) of
- * wq[co,i,j,l,ci] * X(n, t-(kt-1)+i, h-(kh-1)/2+j, w-(kw-1)/2+l, ci), where
+ * q(co,i,j,l,ci) * X(n, t-(kt-1)+i, h-(kh-1)/2+j, w-(kw-1)/2+l, ci), where
  * frames before 0 come from the cache (or are zero) and out-of-image pixels
  * are zero.  Stride 1, dilation 1, "same" spatial padding.
  * Supported: Cin % 32 == 0, Cout % 32 == 0, kt in {1, 3}, (kh, kw) in

@@ -13,6 +13,7 @@ import pytest
 import torch
 
 import oracle
+from tests.layout import pack_weight_codes
 from w8a8_int8_quantized_act_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +116,7 @@ def test_weight_quant_bitexact(ops, shape):
     torch.cuda.synchronize()
     rq, rs = oracle.quantize_weights(w.numpy())
     assert np.array_equal(ws.cpu().numpy().view(np.uint32), rs.view(np.uint32))
-    assert np.array_equal(wq.cpu().numpy(), rq)
+    assert np.array_equal(wq.cpu().numpy(), pack_weight_codes(rq))
 
 
 # ------------------------------------------------------------------ the convolution, small shapes
@@ -155,7 +156,7 @@ def test_conv_small_full(ops, case):
     ref_y = oracle.epilogue(ref_acc, s, ws, ci.b)
 
     xq_d = torch.from_numpy(xq).to(DEV)
-    wq_d = torch.from_numpy(wq).to(DEV)
+    wq_d = torch.from_numpy(pack_weight_codes(wq)).to(DEV)
     cache_d = None if cache is None else torch.from_numpy(cache).to(DEV)
     acc = ops.causalconv3d_w8a8_acc32(xq_d, wq_d, cache_d)
     y = ops.causalconv3d_w8a8(xq_d, torch.tensor([s], device=DEV), wq_d, torch.from_numpy(ws).to(DEV),
@@ -173,7 +174,7 @@ def test_conv_no_bias(ops):
     ci, wq, ws, s, xq, cache = _small_inputs((1, 2, 9, 21, 64, 96, (3, 3, 3), False), 350)
     ref_y = oracle.epilogue(oracle.conv_acc(xq, wq), s, ws, None)
     y = ops.causalconv3d_w8a8(torch.from_numpy(xq).to(DEV), torch.tensor([s], device=DEV),
-                              torch.from_numpy(wq).to(DEV), torch.from_numpy(ws).to(DEV), None)
+                              torch.from_numpy(pack_weight_codes(wq)).to(DEV), torch.from_numpy(ws).to(DEV), None)
     torch.cuda.synchronize()
     assert ulp_dist(bf16_bits(y), ref_y).max() == 0
 
@@ -232,7 +233,7 @@ def _run_full_conv(ops, ci, cache_zero=False):
 def _compare_full(ops, ci, r, n_random=1500, seed=0, cache_zero=False):
     spec = ci.spec
     wq, ws = oracle.quantize_weights(ci.w)
-    assert np.array_equal(r["wq_d"].cpu().numpy(), wq)
+    assert np.array_equal(r["wq_d"].cpu().numpy(), pack_weight_codes(wq))
     assert np.array_equal(r["ws_d"].cpu().numpy().view(np.uint32), ws.view(np.uint32))
     a, s, xq = oracle.act_absmax_quant(ci.x)
     assert int(r["absmax"].item()) == f32_bits(a) >> 16

@@ -156,20 +156,6 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
     }
 }
 
-static int device_cus()
-{
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
-    return cus;
-}
-
 }  // namespace qvae
 
 using namespace qvae;

@@ -14,27 +14,34 @@
 // front padding); out-of-image pixels are zero.  Symmetric quantization has no
 // zero point, so padding is the integer 0.
 //
-// GEMM view: rows = output channels (A = weights, K-contiguous per channel),
-// columns = output pixels (B = activations, channels-last so K = Cin is
-// contiguous per pixel), K = valid temporal taps x kh x kw x Cin.  Nothing is
-// materialised: a workgroup owns a TH x TW pixel tile of one frame and BCO
-// output channels; the K loop runs over "stages" = (valid temporal tap i,
-// 32-channel slice c).  Per stage the workgroup stages in LDS
-//   - the activation halo (TH+kh-1) x (TW+kw-1) pixels x 32 channels of the
-//     frame that tap i reads (zero outside the image), and
-//   - the weights of all kh*kw spatial taps for tap i and slice c,
-// then every wave runs kh*kw x MB x NB v_mfma_i32_32x32x32_i8 on shifted
-// windows of the halo.  Frames that are structurally zero (front padding
-// without a cache) are skipped, not multiplied.  Stages are double-buffered:
-// the global loads of stage s+1 are in flight while stage s computes.
+// GEMM view: rows = output channels (A = weights), columns = output pixels
+// (B = activations, channels-last so K = Cin is contiguous per pixel),
+// K = valid temporal taps x kh x kw x Cin.  Nothing is materialised.
+//
+// Work split.  A workgroup owns a TH x TW pixel tile of one frame and BCO
+// output channels.  Each wave owns MB x NB blocks of 32x32 outputs
+// (MB*32 channels x NB*32 pixels) and, when WK = 2, half of the K range
+// (alternate 32-channel slices); the two K halves are summed through LDS
+// before the epilogue (INT32 sums are exact in any order).
+//
+// K loop.  A "stage" = one valid temporal tap i and SL 32-channel slices.
+// Per stage the workgroup stages in LDS only the activation halo
+// (TH+kh-1) x (TW+kw-1) pixels x 32 channels per slice, zero outside the
+// image; it is reused by all kh*kw spatial taps (shifted windows) and by
+// every wave.  Weights bypass LDS: they are pre-packed in MFMA fragment order
+// (one contiguous 1 KB fragment per 32 channels x 32 K), so each wave loads
+// its own fragments straight from L2 into VGPRs, PD k-steps ahead of use.
+// Frames that are structurally zero (front padding without a cache) are
+// skipped, not multiplied.  Halo stages are double-buffered: the global loads
+// of stage s+1 are in flight while stage s computes.
 //
 // MFMA 32x32x32 i8 operands: lane L supplies 16 bytes of row/column (L % 32)
 // for K-half (L / 32); A and B use the same lane/byte -> k assignment, so the
 // product covers all 32 k of the slice whatever order the hardware sums them
-// in (integer sums are exact).  The INT32 result: lane L holds column L % 32
-// and, in register r, row 8*(r/4) + 4*(L/32) + r%4 -- four consecutive output
-// channels per register quad, so the epilogue writes 4 bf16 (8 bytes) per
-// store along the channels-last output.
+// in.  The INT32 result: lane L holds column L % 32 and, in register r, row
+// 8*(r/4) + 4*(L/32) + r%4 -- four consecutive output channels per register
+// quad, so the epilogue writes 4 bf16 (8 bytes) per store along the
+// channels-last output.
 #include "qvae_internal.h"
 
 namespace qvae {
@@ -45,7 +52,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 struct ConvArgs {
     const int8_t *xq;
     const int8_t *cache;
-    const int8_t *wq;
+    const int8_t *wq;       // packed [Cout/32][kt][Cin/32][kh*kw][64 lanes][16 bytes]
     const float *x_scale;
     const float *w_scale;
     const float *bias;
@@ -55,40 +62,42 @@ struct ConvArgs {
 };
 
 // Halo pixels are stored with a 48-byte pitch (32 data bytes + 16 unused):
-// 3 is odd, so any 8 (or 16) consecutive pixels read by consecutive lanes hit
+// 3 is odd, so 16 consecutive pixels read by 16 consecutive lanes hit 16
 // distinct 16-byte bank groups.
 constexpr int kHaloPitch = 48;
 
-// Weight rows are 32 bytes; the two 16-byte halves of row r are swapped when
-// bit 2 xor bit 3 of r is set, which spreads 8 (or 16) consecutive aligned
-// rows over distinct bank groups.
-__device__ __forceinline__ int wswz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
-
-template <int WM, int WN, int MB, int NB, int TH, int TW, int KH, int KW>
-struct Tile {
-    static constexpr int NT = WM * WN * 64;
-    static constexpr int BCO = WM * MB * 32;
-    static constexpr int BPX = WN * NB * 32;
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_>
+struct ConvCfg {
+    static constexpr int NW = WCO * WPX * WK;
+    static constexpr int NT = NW * 64;
+    static constexpr int BCO = WCO * MB * 32;
+    static constexpr int BPX = WPX * NB * 32;
     static_assert(TH * TW == BPX, "pixel tile must match the wave layout");
-    static_assert(32 % TW == 0 || TW % 32 == 0, "a 32-column MFMA block must tile rows evenly");
+    static_assert(TW == 16 || TW == 32, "a 32-pixel MFMA block covers two rows of 16 or one row of 32");
+    static constexpr int KHW = KH * KW;
+    static constexpr int SPW = SPW_;                         // slices per wave per stage
+    static constexpr int SL = WK * SPW;                      // slices staged per stage
+    static constexpr int KS = KHW * SPW;                     // k-steps per wave per stage
+    static constexpr int PD = (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;   // weight prefetch distance
+    static_assert(KS % PD == 0, "ring slots must repeat per stage");
     static constexpr int HH = TH + KH - 1;
     static constexpr int HWD = TW + KW - 1;
-    static constexpr int HALO_CHUNKS = HH * HWD * 2;        // 16-byte chunks per stage
-    static constexpr int W_CHUNKS = KH * KW * BCO * 2;
-    static constexpr int HALO_BYTES = HH * HWD * kHaloPitch;
-    static constexpr int W_BYTES = KH * KW * BCO * 32;
-    static constexpr int BUF_BYTES = HALO_BYTES + W_BYTES;
+    static constexpr int SLICE_BYTES = HH * HWD * kHaloPitch;
+    static constexpr int BUF_BYTES = SL * SLICE_BYTES;
+    static constexpr int HALO_CHUNKS = SL * HH * HWD * 2;
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
-    static constexpr int W_PT = (W_CHUNKS + NT - 1) / NT;
+    static constexpr int ACC_BYTES = MB * NB * 16 * 64 * 4;  // one wave's accumulators
+    static constexpr int RED_BYTES = (WK > 1) ? WCO * WPX * ACC_BYTES : 0;
+    static constexpr int LDS_BYTES = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
 };
 
-template <int WM, int WN, int MB, int NB, int TH, int TW, int KH, int KW, bool ACC32>
-__global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
+__global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 {
-    using TL = Tile<WM, WN, MB, NB, TH, TW, KH, KW>;
-    constexpr int NT = TL::NT;
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
+    constexpr int NT = C::NT;
     constexpr int PH = (KH - 1) / 2, PW = (KW - 1) / 2;
-    __shared__ __attribute__((aligned(16))) char smem[2 * TL::BUF_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
     // ---- which tile: output-channel tile fastest, so with an even number of
@@ -103,98 +112,95 @@ __global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
     b /= a.tiles_h;
     const int t = b % a.T;
     const int n = b / a.T;
-    const int h0 = thi * TH, w0 = twi * TW, co0 = cot * TL::BCO;
+    const int h0 = thi * TH, w0 = twi * TW, co0 = cot * C::BCO;
     const int H = a.H, W = a.W, Cin = a.Cin, kt = a.kt;
 
     // valid temporal taps: frame t-(kt-1)+i exists, or comes from the cache
     const int i_lo = a.cache ? 0 : max(0, kt - 1 - t);
-    const int nslices = Cin >> 5;
-    const int nst = (kt - i_lo) * nslices;
+    const int S = Cin >> 5;                       // 32-channel slices (a multiple of SL)
+    const int nsp = S / C::SL;                    // stages per temporal tap
+    const int nst = (kt - i_lo) * nsp;
 
-    // ---- per-thread load descriptors (stage independent parts)
-    int h_off[TL::HALO_PT];    // byte offset inside a frame (+ half), -1 = zero / idle
-    int h_lds[TL::HALO_PT];
+    // ---- halo load descriptors (stage independent parts)
+    int h_off[C::HALO_PT];   // byte offset in a frame (+ half), -1 = outside the image
+    int h_lds[C::HALO_PT];   // LDS byte offset inside a stage buffer, -1 = idle lane
+    int h_sl[C::HALO_PT];    // slice within the stage
 #pragma unroll
-    for (int k = 0; k < TL::HALO_PT; ++k) {
+    for (int k = 0; k < C::HALO_PT; ++k) {
         const int u = tid + k * NT;
         h_off[k] = -1;
         h_lds[k] = -1;
-        if (u < TL::HALO_CHUNKS) {
-            const int q = u >> 1, half = u & 1;
-            const int hh = q / TL::HWD, ww = q - hh * TL::HWD;
+        h_sl[k] = 0;
+        if (u < C::HALO_CHUNKS) {
+            const int sl = u / (C::HH * C::HWD * 2);
+            const int r = u - sl * (C::HH * C::HWD * 2);
+            const int q = r >> 1, half = r & 1;
+            const int hh = q / C::HWD, ww = q - hh * C::HWD;
             const int gh = h0 - PH + hh, gw = w0 - PW + ww;
-            h_lds[k] = q * kHaloPitch + half * 16;
+            h_sl[k] = sl;
+            h_lds[k] = sl * C::SLICE_BYTES + q * kHaloPitch + half * 16;
             if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (gh * W + gw) * Cin + half * 16;
         }
     }
-    int w_off[TL::W_PT];       // byte offset into wq for temporal tap 0, slice 0
-    int w_lds[TL::W_PT];
-    const int wrow = kt * KH * KW * Cin;   // bytes per output channel
-#pragma unroll
-    for (int k = 0; k < TL::W_PT; ++k) {
-        const int u = tid + k * NT;
-        w_lds[k] = -1;
-        w_off[k] = 0;
-        if (u < TL::W_CHUNKS) {
-            const int tap = u / (TL::BCO * 2);
-            const int rem = u - tap * (TL::BCO * 2);
-            const int co = rem >> 1, half = rem & 1;
-            w_off[k] = (co0 + co) * wrow + tap * Cin + half * 16;
-            w_lds[k] = (tap * TL::BCO + co) * 32 + ((half ^ wswz(co)) * 16);
-        }
-    }
-
     const size_t frame_bytes = (size_t)H * W * Cin;
     auto frame_ptr = [&](int i) -> const int8_t * {
         const int tau = t - (kt - 1) + i;
         if (tau >= 0) return a.xq + ((size_t)n * a.T + tau) * frame_bytes;
         return a.cache + ((size_t)n * (kt - 1) + (kt - 1 + tau)) * frame_bytes;
     };
-
-    v4i hreg[TL::HALO_PT];
-    v4i wreg[TL::W_PT];
-    auto load_stage = [&](int s) {
-        const int i = i_lo + s / nslices;
-        const int c = s - (s / nslices) * nslices;
-        const int8_t *fp = frame_ptr(i) + c * 32;
-        const int8_t *wp = a.wq + i * KH * KW * Cin + c * 32;
+    v4i hreg[C::HALO_PT];
+    auto load_halo = [&](int st) {
+        const int it = st / nsp;
+        const int p = st - it * nsp;
+        const int8_t *fp = frame_ptr(i_lo + it);
 #pragma unroll
-        for (int k = 0; k < TL::HALO_PT; ++k) {
+        for (int k = 0; k < C::HALO_PT; ++k) {
             hreg[k] = v4i{0, 0, 0, 0};
-            if (h_off[k] >= 0) hreg[k] = *reinterpret_cast<const v4i *>(fp + h_off[k]);
-        }
-#pragma unroll
-        for (int k = 0; k < TL::W_PT; ++k) {
-            if (w_lds[k] >= 0) wreg[k] = *reinterpret_cast<const v4i *>(wp + w_off[k]);
+            const int s = p * C::SL + h_sl[k];
+            if (h_off[k] >= 0) hreg[k] = *reinterpret_cast<const v4i *>(fp + s * 32 + h_off[k]);
         }
     };
-    auto store_stage = [&](int buf) {
-        char *xs = smem + buf * TL::BUF_BYTES;
-        char *ws = xs + TL::HALO_BYTES;
+    auto store_halo = [&](int buf) {
+        char *xs = smem + buf * C::BUF_BYTES;
 #pragma unroll
-        for (int k = 0; k < TL::HALO_PT; ++k)
+        for (int k = 0; k < C::HALO_PT; ++k)
             if (h_lds[k] >= 0) *reinterpret_cast<v4i *>(xs + h_lds[k]) = hreg[k];
-#pragma unroll
-        for (int k = 0; k < TL::W_PT; ++k)
-            if (w_lds[k] >= 0) *reinterpret_cast<v4i *>(ws + w_lds[k]) = wreg[k];
     };
 
-    // ---- per-lane fragment addresses
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave % WM, wn = wave / WM;
+    // ---- wave roles (wave-uniform: keep them in scalar registers so every
+    // branch on them is a scalar branch and the unrolled K loop stays
+    // straight-line code)
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = wave / (WCO * WPX);
+    const int wr = wave - wk * (WCO * WPX);
+    const int wco = wr % WCO, wpx = wr / WCO;
     const int lrow = lane & 31, lhalf = lane >> 5;
-    int a_off[MB];
+
+    // weights: fragment (co block cb, tap i, slice s, spatial tap) at
+    // ((((cb * kt + i) * S + s) * KHW + tap) * 64 + lane) * 16.  Within one
+    // stage a wave walks KS consecutive fragments, so the k-step e of stage st
+    // is at wstage(st) + e * 1 KB.
+    const size_t cb_stride = (size_t)kt * S * C::KHW * 1024;
+    const int8_t *wbase = a.wq + (size_t)(co0 / 32 + wco * MB) * cb_stride + lane * 16;
+    auto wstage = [&](int st) -> const int8_t * {
+        const int it = st / nsp;
+        const int p = st - it * nsp;
+        return wbase + (size_t)(((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
+    };
+    v4i wreg[C::PD][MB];
+    auto load_w = [&](const int8_t *src, int slot) {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int co = wm * MB * 32 + mb * 32 + lrow;
-        a_off[mb] = co * 32 + ((lhalf ^ wswz(co)) * 16);
-    }
+        for (int mb = 0; mb < MB; ++mb) wreg[slot][mb] = *reinterpret_cast<const v4i *>(src + mb * cb_stride);
+    };
+
+    // B fragment base offsets (pixel of lane, within the stage buffer)
     int b_q0[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-        const int p = (wn * NB + nb) * 32 + lrow;
+        const int p = (wpx * NB + nb) * 32 + lrow;
         const int pr = p / TW, pc = p - pr * TW;
-        b_q0[nb] = (pr * TL::HWD + pc) * kHaloPitch + lhalf * 16;
+        b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + lhalf * 16 + wk * C::SPW * C::SLICE_BYTES;
     }
 
     v16i acc[MB][NB];
@@ -203,37 +209,91 @@ __global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
 
-    if (nst > 0) {
-        load_stage(0);
-        store_stage(0);
-    }
+    const int8_t *wcur = wstage(0);
+#pragma unroll
+    for (int e = 0; e < C::PD; ++e) load_w(wcur + e * 1024, e);
+    load_halo(0);
+    store_halo(0);
     __syncthreads();
-    for (int s = 0; s < nst; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < nst) load_stage(s + 1);
-        const char *xs = smem + buf * TL::BUF_BYTES;
-        const char *ws = xs + TL::HALO_BYTES;
+
+    // B fragments of k-step e of the stage held in buffer xs
+    auto read_b = [&](const char *xs, int e, v4i (&bv)[NB]) {
+        const int sp = e / C::KHW, tap = e % C::KHW;
+        const int j = tap / KW, l = tap % KW;
+        const char *xsl = xs + sp * C::SLICE_BYTES + (j * C::HWD + l) * kHaloPitch;
 #pragma unroll
-        for (int j = 0; j < KH; ++j) {
+        for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
+    };
+
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        const bool more = st + 1 < nst;
+        // the next stage's weights (the current ones again after the last
+        // stage: harmless reads, no branch in the loop body)
+        const int8_t *wnext = wstage(more ? st + 1 : st);
+        if (more) load_halo(st + 1);
+        const char *xs = smem + buf * C::BUF_BYTES;
+        v4i bcur[NB], bnext[NB];
+        read_b(xs, 0, bcur);
+        // Each k-step: LDS reads of the next step's B fragments (issued first,
+        // so they land while this step's MFMAs run), the MB x NB MFMAs of this
+        // step, then the weight loads PD steps ahead into the ring slot just
+        // consumed.  The scheduling barriers keep every load in the step it
+        // was issued in (the scheduler would otherwise sink the prefetches
+        // down to their use and expose the L2 latency).
 #pragma unroll
-            for (int l = 0; l < KW; ++l) {
-                const int tap = j * KW + l;
-                v4i av[MB], bv[NB];
+        for (int e = 0; e < C::KS; ++e) {
+            const int slot = e % C::PD;
+            if (e + 1 < C::KS) read_b(xs, e + 1, bnext);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-                    av[mb] = *reinterpret_cast<const v4i *>(ws + tap * TL::BCO * 32 + a_off[mb]);
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    bv[nb] = *reinterpret_cast<const v4i *>(xs + b_q0[nb] + (j * TL::HWD + l) * kHaloPitch);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+            if (e + C::PD < C::KS)
+                load_w(wcur + (e + C::PD) * 1024, slot);
+            else
+                load_w(wnext + (e + C::PD - C::KS) * 1024, slot);
+            __builtin_amdgcn_sched_barrier(0);
+            if (e + 1 < C::KS) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+                for (int nb = 0; nb < NB; ++nb) bcur[nb] = bnext[nb];
             }
         }
-        if (s + 1 < nst) store_stage(buf ^ 1);
+        if (more) store_halo(buf ^ 1);
         __syncthreads();
+        wcur = wnext;
+    }
+
+    // ---- split-K: the second K half hands its sums to the first through LDS
+    if constexpr (WK > 1) {
+        int4 *red = reinterpret_cast<int4 *>(smem + wr * C::ACC_BYTES);
+        if (wk == 1) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        red[((mb * NB + nb) * 4 + g) * 64 + lane] =
+                            make_int4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
+                                      acc[mb][nb][4 * g + 3]);
+        }
+        __syncthreads();
+        if (wk == 1) return;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int4 v = red[((mb * NB + nb) * 4 + g) * 64 + lane];
+                    acc[mb][nb][4 * g] += v.x;
+                    acc[mb][nb][4 * g + 1] += v.y;
+                    acc[mb][nb][4 * g + 2] += v.z;
+                    acc[mb][nb][4 * g + 3] += v.w;
+                }
     }
 
     // ---- epilogue: lane holds pixel (column) lrow of each 32-pixel block and
@@ -245,7 +305,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const int co = co0 + wm * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
+            const int co = co0 + (wco * MB + mb) * 32 + g * 8 + lhalf * 4;
             float m[4], bb[4];
             if (!ACC32) {
 #pragma unroll
@@ -256,7 +316,7 @@ __global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
             }
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int p = (wn * NB + nb) * 32 + lrow;
+                const int p = (wpx * NB + nb) * 32 + lrow;
                 const int pr = p / TW, pc = p - pr * TW;
                 const int gh = h0 + pr, gw = w0 + pc;
                 if (gh < H && gw < W) {
@@ -283,32 +343,58 @@ __global__ __launch_bounds__(WM *WN * 64) void k_conv_igemm(ConvArgs a)
 
 // ---- host side ------------------------------------------------------------
 
-template <int WM, int WN, int MB, int NB, int TH, int TW, int KH, int KW>
-static int launch_tile(const ConvArgs &base, bool acc32, hipStream_t st)
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
+static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
 {
-    using TL = Tile<WM, WN, MB, NB, TH, TW, KH, KW>;
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     ConvArgs a = base;
+    if ((a.Cin / 32) % C::SL != 0) return QVAE_EUNSUPPORTED;   // (the dispatcher never asks)
     a.tiles_w = (a.W + TW - 1) / TW;
     a.tiles_h = (a.H + TH - 1) / TH;
-    a.co_tiles = a.Cout / TL::BCO;
+    a.co_tiles = a.Cout / C::BCO;
     const int64_t blocks = (int64_t)a.co_tiles * a.tiles_w * a.tiles_h * a.T * a.N;
     if (blocks <= 0 || blocks > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
     if (acc32)
-        hipLaunchKernelGGL((k_conv_igemm<WM, WN, MB, NB, TH, TW, KH, KW, true>), dim3((unsigned)blocks),
-                           dim3(TL::NT), 0, st, a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>),
+                           dim3((unsigned)blocks), dim3(C::NT), 0, st, a);
     else
-        hipLaunchKernelGGL((k_conv_igemm<WM, WN, MB, NB, TH, TW, KH, KW, false>), dim3((unsigned)blocks),
-                           dim3(TL::NT), 0, st, a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>),
+                           dim3((unsigned)blocks), dim3(C::NT), 0, st, a);
     return launch_status();
 }
 
-template <int KH, int KW>
+static int64_t px_tiles(const ConvArgs &a, int th, int tw)
+{
+    return (int64_t)((a.H + th - 1) / th) * ((a.W + tw - 1) / tw) * a.T * a.N;
+}
+
+// Tile choice: the largest per-wave tile (3 x 4 blocks of 32x32 = 96 channels
+// x 128 pixels) whenever the channel count allows; split K inside the
+// workgroup when there are too few pixel tiles to give every CU a
+// workgroup.  1x1 kernels stage two slices per wave per stage when the slice
+// count allows it, so a stage still holds more than one k-step.
+template <int KH, int KW, int SPW>
 static int launch_spatial(const ConvArgs &a, bool acc32, hipStream_t st)
 {
-    if (a.Cout % 192 == 0) return launch_tile<2, 2, 3, 2, 8, 16, KH, KW>(a, acc32, st);
-    if (a.Cout % 96 == 0) return launch_tile<1, 4, 3, 2, 16, 16, KH, KW>(a, acc32, st);
-    if (a.Cout % 64 == 0) return launch_tile<2, 2, 1, 2, 8, 16, KH, KW>(a, acc32, st);
-    return launch_tile<1, 4, 1, 2, 16, 16, KH, KW>(a, acc32, st);
+    const int64_t cus = device_cus();
+    const int S = a.Cin / 32;
+    const bool k2 = S % (2 * SPW) == 0;   // the K range splits into two equal halves
+    if (a.Cout % 96 == 0) {
+        if (a.Cout % 384 == 0 && (px_tiles(a, 8, 16) * (a.Cout / 384) >= cus || !k2))
+            return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+        if (a.Cout % 192 == 0 && (px_tiles(a, 16, 16) * (a.Cout / 192) >= cus || !k2))
+            return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
+        if (a.Cout % 192 == 0) return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+        if constexpr (KH * KW > 1) {
+            if (px_tiles(a, 16, 32) * (a.Cout / 96) >= cus || !k2)
+                return launch_cfg<1, 4, 1, 3, 4, 16, 32, KH, KW, SPW>(a, acc32, st);
+        } else {
+            if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
+                return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
+        }
+        return launch_cfg<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+    }
+    return launch_cfg<1, 2, 1, 1, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
 }
 
 static int conv_validate(const int8_t *xq, const int8_t *wq, const void *out, int N, int T, int H, int W,
@@ -317,23 +403,23 @@ static int conv_validate(const int8_t *xq, const int8_t *wq, const void *out, in
     if (!xq || !wq || !out) return QVAE_EINVAL;
     if (N <= 0 || T <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || kt <= 0 || kh <= 0 || kw <= 0)
         return QVAE_EINVAL;
-    if (!aligned16(xq) || !aligned16(out) || (cache && !aligned16(cache))) return QVAE_EINVAL;
+    if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (cache && !aligned16(cache))) return QVAE_EINVAL;
     if (Cin % 32 != 0 || Cout % 32 != 0) return QVAE_EUNSUPPORTED;
     if (kt != 1 && kt != 3) return QVAE_EUNSUPPORTED;
     if (!((kh == 1 && kw == 1) || (kh == 3 && kw == 3))) return QVAE_EUNSUPPORTED;
     // |acc| <= 127^2 * K must stay inside int32
     const int64_t K = (int64_t)Cin * kt * kh * kw;
     if (K * 127 * 127 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
-    // byte offsets inside one frame and one weight row are 32-bit
+    // byte offsets inside one frame are 32-bit
     if ((int64_t)H * W * Cin >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
-    if ((int64_t)Cout * K >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
     return QVAE_OK;
 }
 
 static int conv_dispatch(const ConvArgs &a, int kh, bool acc32, hipStream_t st)
 {
-    if (kh == 3) return launch_spatial<3, 3>(a, acc32, st);
-    return launch_spatial<1, 1>(a, acc32, st);
+    if (kh == 3) return launch_spatial<3, 3, 1>(a, acc32, st);
+    if ((a.Cin / 32) % 2 == 0) return launch_spatial<1, 1, 2>(a, acc32, st);
+    return launch_spatial<1, 1, 1>(a, acc32, st);
 }
 
 }  // namespace qvae

@@ -27,6 +27,21 @@ inline int launch_status()
     return e == hipSuccess ? QVAE_OK : QVAE_ELAUNCH;
 }
 
+// Compute units of the current device (queried once; 256 on MI355X).
+inline int device_cus()
+{
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
+}
+
 // ---- device helpers -------------------------------------------------------
 
 // bf16 bit pattern -> float (exact widening).

@@ -8,8 +8,12 @@
 // Runs once per layer at load time.  One workgroup per output channel: a
 // max-reduction over the channel (non-negative floats compare like their bit
 // patterns, so the DPP integer max applies), then every lane quantizes and
-// scatters into the K-contiguous layout [Cout][kt][kh][kw][Cin] the
-// convolution reads.
+// scatters into the layout the convolution consumes: MFMA fragments of 32
+// output channels x 32 input channels, one contiguous kilobyte each, in the
+// order the K loop walks them,
+//   wq[co/32][i][ci/32][j*kw + l][lane][byte],  lane = 32*((ci%32)/16) + co%32,
+//   byte = ci % 16,
+// so a wave fetches one fragment with one fully coalesced 16-byte-per-lane load.
 #include "qvae_internal.h"
 
 namespace qvae {
@@ -44,19 +48,26 @@ __global__ __launch_bounds__(kWqThreads) void k_quantize_weights(const float *__
     }
     __syncthreads();
     const float s = s_sh;
+    const bool s_pos = s > 0.0f;
 
-    // source order [ci][tap] (tap = (i*kh + j)*kw + l); destination [tap][ci]
-    int8_t *dst = wq + (int64_t)co * per_co;
+    // source order [ci][i][j][l]; destination: packed fragments (see above)
+    const int khw = kh * kw;
+    const int S = Cin >> 5;
+    const int cb = co >> 5, row = co & 31;
     for (int64_t e = threadIdx.x; e < per_co; e += kWqThreads) {
         const int ci = (int)(e / taps);
         const int tap = (int)(e - (int64_t)ci * taps);
+        const int i = tap / khw, sp = tap - i * khw;
+        const int sl = ci >> 5, c = ci & 31;
+        const int lane = (c >> 4) * 32 + row;
         int q = 0;
-        if (s > 0.0f) {
-            float t = wc[e] / s;   // correctly rounded division
-            t = fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f);
-            q = (int)t;
+        if (s_pos) {
+            float v = wc[e] / s;   // correctly rounded division
+            v = fminf(fmaxf(__builtin_rintf(v), -127.0f), 127.0f);
+            q = (int)v;
         }
-        dst[(int64_t)tap * Cin + ci] = (int8_t)q;
+        const int64_t dst = ((((int64_t)cb * kt + i) * S + sl) * khw + sp) * 1024 + lane * 16 + (c & 15);
+        wq[dst] = (int8_t)q;
     }
 }
 
@@ -72,6 +83,8 @@ extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, 
         return QVAE_EINVAL;
     if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
     if ((kt != 1 && kt != 3) || (kh != 1 && kh != 3) || (kw != 1 && kw != 3)) return QVAE_EUNSUPPORTED;
+    if (Cout % 32 != 0 || Cin % 32 != 0) return QVAE_EUNSUPPORTED;
+    if (!aligned16(wq)) return QVAE_EINVAL;
     hipLaunchKernelGGL(k_quantize_weights, dim3(Cout), dim3(kWqThreads), 0, as_stream(stream), w, Cin,
                        kt, kh, kw, clip_ratio, wq, w_scale);
     return launch_status();

@@ -96,11 +96,19 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
 
 
 # ------------------------------------------------------------------ weights
+def packed_weight_shape(Cout, Cin, kt, kh, kw):
+    """Shape of the packed INT8 weights: [Cout/32][kt][Cin/32][kh][kw][64][16]."""
+    return (Cout // 32, kt, Cin // 32, kh, kw, 64, 16)
+
+
 def quantize_weights(w: torch.Tensor, clip_ratio: float = 1.0, stream=None):
-    """w float32 [Cout][Cin][kt][kh][kw] -> (wq int8 [Cout][kt][kh][kw][Cin], w_scale float32 [Cout])."""
+    """w float32 [Cout][Cin][kt][kh][kw] -> (wq int8 packed [Cout/32][kt][Cin/32][kh][kw][64][16],
+    w_scale float32 [Cout]); see qvae.h for the packing."""
     _dev(w, "w", torch.float32)
     Cout, Cin, kt, kh, kw = w.shape
-    wq = torch.empty((Cout, kt, kh, kw, Cin), dtype=torch.int8, device=w.device)
+    if Cout % 32 or Cin % 32:
+        raise QvaeError(EUNSUPPORTED, "quantize_weights: Cout and Cin must be multiples of 32")
+    wq = torch.empty(packed_weight_shape(Cout, Cin, kt, kh, kw), dtype=torch.int8, device=w.device)
     ws = torch.empty((Cout,), dtype=torch.float32, device=w.device)
     _check(lib().qvae_quantize_weights(_p(w), Cout, Cin, kt, kh, kw, float(clip_ratio),
                                        _p(wq), _p(ws), _stream(stream)), "qvae_quantize_weights")
@@ -157,7 +165,9 @@ def _conv_dims(xq, wq, cache):
     _dev(xq, "xq", torch.int8)
     _dev(wq, "wq", torch.int8)
     N, T, H, W, Cin = xq.shape
-    Cout, kt, kh, kw, Cin2 = wq.shape
+    if wq.dim() != 7 or tuple(wq.shape[5:]) != (64, 16):
+        raise ValueError("wq must be the packed [Cout/32][kt][Cin/32][kh][kw][64][16] tensor")
+    Cout, kt, Cin2, kh, kw = wq.shape[0] * 32, wq.shape[1], wq.shape[2] * 32, wq.shape[3], wq.shape[4]
     if Cin2 != Cin:
         raise ValueError(f"Cin mismatch: xq has {Cin}, wq has {Cin2}")
     if cache is not None:
