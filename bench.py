@@ -116,7 +116,20 @@ def main():
     ap.add_argument("--level", type=int, default=0, help="layer index inside a level sweep")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the W8A8 CausalConv3d path here runs on a single MI355X "

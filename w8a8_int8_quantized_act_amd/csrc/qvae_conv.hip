@@ -80,6 +80,7 @@ struct ConvCfg {
     static constexpr int KS = KHW * SPW;                     // k-steps per wave per stage
     static constexpr int PD = (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;   // weight prefetch distance
     static_assert(KS % PD == 0, "ring slots must repeat per stage");
+    static constexpr int HALO_STORE_STEP = (PD < KS) ? PD : KS - 1;
     static constexpr int HH = TH + KH - 1;
     static constexpr int HWD = TW + KW - 1;
     static constexpr int SLICE_BYTES = HH * HWD * kHaloPitch;
@@ -88,7 +89,11 @@ struct ConvCfg {
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
     static constexpr int ACC_BYTES = MB * NB * 16 * 64 * 4;  // one wave's accumulators
     static constexpr int RED_BYTES = (WK > 1) ? WCO * WPX * ACC_BYTES : 0;
-    static constexpr int LDS_BYTES = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
+    // epilogue staging: 32 pixel rows of one wave's channels (INT32 worst case)
+    static constexpr int EPI_WAVE_BYTES = 32 * (MB * 32 * 4 + 16);
+    static constexpr int EPI_BYTES = WCO * WPX * EPI_WAVE_BYTES;
+    static constexpr int LDS_MAIN = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
+    static constexpr int LDS_BYTES = (LDS_MAIN > EPI_BYTES) ? LDS_MAIN : EPI_BYTES;
 };
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     for (int e = 0; e < C::PD; ++e) load_w(wcur + e * 1024, e);
     load_halo(0);
     store_halo(0);
-    __syncthreads();
+    lds_barrier();
 
     // B fragments of k-step e of the stage held in buffer xs
     auto read_b = [&](const char *xs, int e, v4i (&bv)[NB]) {
@@ -255,14 +260,18 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                 load_w(wcur + (e + C::PD) * 1024, slot);
             else
                 load_w(wnext + (e + C::PD - C::KS) * 1024, slot);
+            // The next stage's halo goes to the other buffer as soon as its
+            // loads are covered by a wait this step needs anyway (they were
+            // issued before the weights of step PD); nobody reads that buffer
+            // after the previous stage's barrier.
+            if (e == C::HALO_STORE_STEP && more) store_halo(buf ^ 1);
             __builtin_amdgcn_sched_barrier(0);
             if (e + 1 < C::KS) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) bcur[nb] = bnext[nb];
             }
         }
-        if (more) store_halo(buf ^ 1);
-        __syncthreads();
+        lds_barrier();
         wcur = wnext;
     }
 
@@ -296,46 +305,69 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                 }
     }
 
-    // ---- epilogue: lane holds pixel (column) lrow of each 32-pixel block and
-    // output channels 8*g + 4*lhalf + {0..3} of each 32-channel block.
+    // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
+    // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
+    // block.  Each 32-pixel block is rescaled (FP32 fma with the per-channel
+    // factor and bias, bf16 round-to-nearest-even), written to the wave's own
+    // LDS staging rows [pixel][channel], then read back row-wise so every lane
+    // stores 16 contiguous bytes and consecutive lanes continue along the
+    // channels-last output row.
+    constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
+    constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
+    constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
+    constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
+    static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
+    static_assert(32 * EPITCH <= C::EPI_WAVE_BYTES, "staging rows fit the wave's LDS slice");
+    char *stage = smem + (WK > 1 ? wr * C::ACC_BYTES : wr * C::EPI_WAVE_BYTES);
+
     const size_t pix_base = ((size_t)n * a.T + t) * H;
-    float sx = 0.0f;
-    if (!ACC32) sx = *a.x_scale;
+    const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
+    float m[MB][4][4], bb[MB][4][4];
+    if (!ACC32) {
+        const float sx = *a.x_scale;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int co = co0 + (wco * MB + mb) * 32 + g * 8 + lhalf * 4;
-            float m[4], bb[4];
-            if (!ACC32) {
+            for (int g = 0; g < 4; ++g)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    m[e] = sx * a.w_scale[co + e];
-                    bb[e] = a.bias ? a.bias[co + e] : 0.0f;
+                    const int co = cw0 + mb * 32 + g * 8 + lhalf * 4 + e;
+                    m[mb][g][e] = sx * a.w_scale[co];
+                    bb[mb][g][e] = a.bias ? a.bias[co] : 0.0f;
+                }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
+                if constexpr (ACC32) {
+                    *reinterpret_cast<v4i *>(dst) = v4i{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
+                                                        acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]};
+                } else {
+                    uint32_t h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        h[e] = float_to_bf16_bits(
+                            __builtin_fmaf((float)acc[mb][nb][4 * g + e], m[mb][g][e], bb[mb][g][e]));
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                 }
             }
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int p = (wpx * NB + nb) * 32 + lrow;
-                const int pr = p / TW, pc = p - pr * TW;
-                const int gh = h0 + pr, gw = w0 + pc;
-                if (gh < H && gw < W) {
-                    const size_t o = ((pix_base + gh) * W + gw) * (size_t)a.Cout + co;
-                    if (ACC32) {
-                        v4i v = {acc[mb][nb][g * 4 + 0], acc[mb][nb][g * 4 + 1], acc[mb][nb][g * 4 + 2],
-                                 acc[mb][nb][g * 4 + 3]};
-                        *reinterpret_cast<v4i *>(static_cast<int32_t *>(a.out) + o) = v;
-                    } else {
-                        uint32_t h[4];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float y = __builtin_fmaf((float)acc[mb][nb][g * 4 + e], m[e], bb[e]);
-                            h[e] = float_to_bf16_bits(y);
-                        }
-                        uint2 v = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + o) = v;
-                    }
-                }
+        for (int k = 0; k < CHUNKS / 64; ++k) {
+            const int c = k * 64 + lane;
+            const int px = c / (ROWB / 16);
+            const int off = (c - px * (ROWB / 16)) * 16;
+            const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
+            const int p = (wpx * NB + nb) * 32 + px;
+            const int pr = p / TW, pc = p - pr * TW;
+            const int gh = h0 + pr, gw = w0 + pc;
+            if (gh < H && gw < W) {
+                char *o = static_cast<char *>(a.out) +
+                          (((pix_base + gh) * W + gw) * (size_t)a.Cout + cw0) * ELEM + off;
+                *reinterpret_cast<v4i *>(o) = v;
             }
         }
     }

@@ -58,6 +58,16 @@ __device__ __forceinline__ uint32_t float_to_bf16_bits(float f)
     return u >> 16;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load of the wave (vmcnt(0)), which would drain the
+// weight prefetches in flight; the K loop only communicates through LDS.
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Maximum of an unsigned value over the 64 lanes of a wavefront: DPP
 // exchanges inside each row of 16 lanes, then the four row results are read
 // with readlane.  Every lane returns the wave maximum.
