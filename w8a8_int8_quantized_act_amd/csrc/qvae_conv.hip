@@ -42,6 +42,8 @@
 // 8*(r/4) + 4*(L/32) + r%4 -- four consecutive output channels per register
 // quad, so the epilogue writes 4 bf16 (8 bytes) per store along the
 // channels-last output.
+#include <type_traits>
+
 #include "qvae_internal.h"
 
 namespace qvae {
@@ -88,12 +90,18 @@ struct ConvCfg {
     static constexpr int HALO_CHUNKS = SL * HH * HWD * 2;
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
     static constexpr int ACC_BYTES = MB * NB * 16 * 64 * 4;  // one wave's accumulators
-    static constexpr int RED_BYTES = (WK > 1) ? WCO * WPX * ACC_BYTES : 0;
+    // split K: each wave exports the half of its blocks its partner finishes
+    static constexpr int XB = ACC_BYTES / 2;
+    static constexpr int RED_BYTES = (WK > 1) ? WCO * WPX * 2 * XB : 0;
+    static_assert(WK == 1 || NB % 2 == 0, "split K shares the pixel blocks between the two halves");
     // epilogue staging: 32 pixel rows of one wave's channels (INT32 worst case)
     static constexpr int EPI_WAVE_BYTES = 32 * (MB * 32 * 4 + 16);
     static constexpr int EPI_BYTES = WCO * WPX * EPI_WAVE_BYTES;
     static constexpr int LDS_MAIN = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
-    static constexpr int LDS_BYTES = (LDS_MAIN > EPI_BYTES) ? LDS_MAIN : EPI_BYTES;
+    static constexpr int LDS_WORK = (LDS_MAIN > EPI_BYTES) ? LDS_MAIN : EPI_BYTES;
+    // per-channel rescale factors fl(s_x * s_w[co]) and biases of the tile
+    static constexpr int FAC_BYTES = 2 * BCO * 4;
+    static constexpr int LDS_BYTES = LDS_WORK + FAC_BYTES;
 };
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
@@ -214,11 +222,40 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
 
+    // rescale factors and biases of this tile's channels (for the epilogue):
+    // loaded first, stored to LDS once the prologue's own waits cover them
+    constexpr int FPT = (C::BCO + NT - 1) / NT;
+    float *s_fac = reinterpret_cast<float *>(smem + C::LDS_WORK);
+    float fac_s[FPT], fac_b[FPT];
+    if constexpr (!ACC32) {
+        const float sx = *a.x_scale;
+#pragma unroll
+        for (int k = 0; k < FPT; ++k) {
+            const int c = tid + k * NT;
+            fac_s[k] = 0.0f;
+            fac_b[k] = 0.0f;
+            if (c < C::BCO) {
+                fac_s[k] = sx * a.w_scale[co0 + c];
+                if (a.bias) fac_b[k] = a.bias[co0 + c];
+            }
+        }
+    }
+
     const int8_t *wcur = wstage(0);
 #pragma unroll
     for (int e = 0; e < C::PD; ++e) load_w(wcur + e * 1024, e);
     load_halo(0);
     store_halo(0);
+    if constexpr (!ACC32) {
+#pragma unroll
+        for (int k = 0; k < FPT; ++k) {
+            const int c = tid + k * NT;
+            if (c < C::BCO) {
+                s_fac[c] = fac_s[k];
+                s_fac[C::BCO + c] = fac_b[k];
+            }
+        }
+    }
     lds_barrier();
 
     // B fragments of k-step e of the stage held in buffer xs
@@ -275,84 +312,99 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         wcur = wnext;
     }
 
-    // ---- split-K: the second K half hands its sums to the first through LDS
+    // ---- split K: each half finishes half of the pixel blocks.  Wave wk
+    // exports to LDS the blocks the other half finishes, then adds the
+    // other half's export of its own blocks (INT32 sums, exact in any order).
     if constexpr (WK > 1) {
-        int4 *red = reinterpret_cast<int4 *>(smem + wr * C::ACC_BYTES);
-        if (wk == 1) {
+        constexpr int HB = NB / 2;
+        auto xchg = [&](auto wkc) {
+            constexpr int me = decltype(wkc)::value, other = 1 - me;
+            int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + me) * C::XB);
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
+                for (int j = 0; j < HB; ++j)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        red[((mb * NB + nb) * 4 + g) * 64 + lane] =
-                            make_int4(acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1], acc[mb][nb][4 * g + 2],
-                                      acc[mb][nb][4 * g + 3]);
-        }
-        __syncthreads();
-        if (wk == 1) return;
+                    for (int g = 0; g < 4; ++g) {
+                        const v16i &v = acc[mb][other * HB + j];
+                        exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
+                            make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                    }
+            __syncthreads();
+            const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + other) * C::XB);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+                for (int j = 0; j < HB; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int4 v = red[((mb * NB + nb) * 4 + g) * 64 + lane];
-                    acc[mb][nb][4 * g] += v.x;
-                    acc[mb][nb][4 * g + 1] += v.y;
-                    acc[mb][nb][4 * g + 2] += v.z;
-                    acc[mb][nb][4 * g + 3] += v.w;
-                }
+                    for (int g = 0; g < 4; ++g) {
+                        const int4 u = exp_other[((mb * HB + j) * 4 + g) * 64 + lane];
+                        v16i &v = acc[mb][me * HB + j];
+                        v[4 * g] += u.x;
+                        v[4 * g + 1] += u.y;
+                        v[4 * g + 2] += u.z;
+                        v[4 * g + 3] += u.w;
+                    }
+        };
+        if (wk == 0)
+            xchg(std::integral_constant<int, 0>{});
+        else
+            xchg(std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
     // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
-    // block.  Each 32-pixel block is rescaled (FP32 fma with the per-channel
-    // factor and bias, bf16 round-to-nearest-even), written to the wave's own
-    // LDS staging rows [pixel][channel], then read back row-wise so every lane
-    // stores 16 contiguous bytes and consecutive lanes continue along the
-    // channels-last output row.
+    // block.  Each 32-pixel block is rescaled (one FP32 fma with the
+    // per-channel factor and bias, then bf16 round-to-nearest-even with the
+    // packed convert), written to the wave's LDS staging rows
+    // [pixel][channel], then read back row-wise so every lane stores 16
+    // contiguous bytes and consecutive lanes continue along the channels-last
+    // output row.
     constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
     constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
     constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
     constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
     static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
     static_assert(32 * EPITCH <= C::EPI_WAVE_BYTES, "staging rows fit the wave's LDS slice");
-    char *stage = smem + (WK > 1 ? wr * C::ACC_BYTES : wr * C::EPI_WAVE_BYTES);
+    static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
+    // staging: with split K the partner's export slice (this wave has read it
+    // and nobody else touches it); otherwise a slice per wave
+    char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : wr * C::EPI_WAVE_BYTES);
 
     const size_t pix_base = ((size_t)n * a.T + t) * H;
     const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
-    float m[MB][4][4], bb[MB][4][4];
-    if (!ACC32) {
-        const float sx = *a.x_scale;
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+    f4 fm[MB][4], fb[MB][4];
+    if constexpr (!ACC32) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int co = cw0 + mb * 32 + g * 8 + lhalf * 4 + e;
-                    m[mb][g][e] = sx * a.w_scale[co];
-                    bb[mb][g][e] = a.bias ? a.bias[co] : 0.0f;
-                }
+            for (int g = 0; g < 4; ++g) {
+                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
+                fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
+                fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
+            }
     }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    auto finish_block = [&](int nb, const v16i (&accb)[MB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
                 if constexpr (ACC32) {
-                    *reinterpret_cast<v4i *>(dst) = v4i{acc[mb][nb][4 * g], acc[mb][nb][4 * g + 1],
-                                                        acc[mb][nb][4 * g + 2], acc[mb][nb][4 * g + 3]};
+                    *reinterpret_cast<v4i *>(dst) =
+                        v4i{accb[mb][4 * g], accb[mb][4 * g + 1], accb[mb][4 * g + 2], accb[mb][4 * g + 3]};
                 } else {
-                    uint32_t h[4];
+                    f4 y;
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        h[e] = float_to_bf16_bits(
-                            __builtin_fmaf((float)acc[mb][nb][4 * g + e], m[mb][g][e], bb[mb][g][e]));
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                        y[e] = __builtin_fmaf((float)accb[mb][4 * g + e], fm[mb][g][e], fb[mb][g][e]);
+                    const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
+                    const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+                    *reinterpret_cast<uint2 *>(dst) =
+                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
                 }
             }
 #pragma unroll
@@ -370,6 +422,24 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                 *reinterpret_cast<v4i *>(o) = v;
             }
         }
+    };
+    auto finish_range = [&](auto lo_c, auto hi_c) {
+        constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+#pragma unroll
+        for (int nb = lo; nb < hi; ++nb) {
+            v16i accb[MB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) accb[mb] = acc[mb][nb];
+            finish_block(nb, accb);
+        }
+    };
+    if constexpr (WK > 1) {
+        if (wk == 0)
+            finish_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NB / 2>{});
+        else
+            finish_range(std::integral_constant<int, NB / 2>{}, std::integral_constant<int, NB>{});
+    } else {
+        finish_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NB>{});
     }
 }
 
