@@ -85,7 +85,9 @@ struct ConvCfg {
     static constexpr int HALO_STORE_STEP = (PD < KS) ? PD : KS - 1;
     static constexpr int HH = TH + KH - 1;
     static constexpr int HWD = TW + KW - 1;
-    static constexpr int SLICE_BYTES = HH * HWD * kHaloPitch;
+    // one 32-channel slice of the halo; slices are 32 bytes apart modulo 128
+    // so the chunks of one pixel written by consecutive lanes spread over banks
+    static constexpr int SLICE_BYTES = (HH * HWD * kHaloPitch + 127) / 128 * 128 + 32;
     static constexpr int BUF_BYTES = SL * SLICE_BYTES;
     static constexpr int HALO_CHUNKS = SL * HH * HWD * 2;
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
@@ -134,25 +136,23 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     const int nsp = S / C::SL;                    // stages per temporal tap
     const int nst = (kt - i_lo) * nsp;
 
-    // ---- halo load descriptors (stage independent parts)
-    int h_off[C::HALO_PT];   // byte offset in a frame (+ half), -1 = outside the image
+    // ---- halo load descriptors (stage independent parts).  Chunk u covers
+    // pixel q = u / (2*SL) and 16 bytes c = u % (2*SL) of its SL slices, so
+    // consecutive lanes read each pixel's 32*SL contiguous bytes together.
+    int h_off[C::HALO_PT];   // byte offset in a frame, -1 = outside the image
     int h_lds[C::HALO_PT];   // LDS byte offset inside a stage buffer, -1 = idle lane
-    int h_sl[C::HALO_PT];    // slice within the stage
 #pragma unroll
     for (int k = 0; k < C::HALO_PT; ++k) {
         const int u = tid + k * NT;
         h_off[k] = -1;
         h_lds[k] = -1;
-        h_sl[k] = 0;
         if (u < C::HALO_CHUNKS) {
-            const int sl = u / (C::HH * C::HWD * 2);
-            const int r = u - sl * (C::HH * C::HWD * 2);
-            const int q = r >> 1, half = r & 1;
+            const int q = u / (2 * C::SL), c = u - q * (2 * C::SL);
+            const int sl = c >> 1, half = c & 1;
             const int hh = q / C::HWD, ww = q - hh * C::HWD;
             const int gh = h0 - PH + hh, gw = w0 - PW + ww;
-            h_sl[k] = sl;
             h_lds[k] = sl * C::SLICE_BYTES + q * kHaloPitch + half * 16;
-            if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (gh * W + gw) * Cin + half * 16;
+            if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (gh * W + gw) * Cin + c * 16;
         }
     }
     const size_t frame_bytes = (size_t)H * W * Cin;
@@ -166,11 +166,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         const int it = st / nsp;
         const int p = st - it * nsp;
         const int8_t *fp = frame_ptr(i_lo + it);
+        const int8_t *fps = fp + p * C::SL * 32;
 #pragma unroll
         for (int k = 0; k < C::HALO_PT; ++k) {
             hreg[k] = v4i{0, 0, 0, 0};
-            const int s = p * C::SL + h_sl[k];
-            if (h_off[k] >= 0) hreg[k] = *reinterpret_cast<const v4i *>(fp + s * 32 + h_off[k]);
+            if (h_off[k] >= 0) hreg[k] = *reinterpret_cast<const v4i *>(fps + h_off[k]);
         }
     };
     auto store_halo = [&](int buf) {
@@ -519,6 +519,9 @@ static int conv_validate(const int8_t *xq, const int8_t *wq, const void *out, in
 
 static int conv_dispatch(const ConvArgs &a, int kh, bool acc32, hipStream_t st)
 {
+    // two 32-channel slices per wave and stage when the slice count is even:
+    // half the stages (barriers) and 64 contiguous bytes per halo pixel load
+    if (kh == 3 && (a.Cin / 32) % 2 == 0) return launch_spatial<3, 3, 2>(a, acc32, st);
     if (kh == 3) return launch_spatial<3, 3, 1>(a, acc32, st);
     if ((a.Cin / 32) % 2 == 0) return launch_spatial<1, 1, 2>(a, acc32, st);
     return launch_spatial<1, 1, 1>(a, acc32, st);
