@@ -159,7 +159,7 @@ def main():
     b = torch.from_numpy(ci.b).to(dev)
     cache = (torch.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), dtype=torch.int8, device=dev)
              if use_cache else None)
-    absmax = torch.empty((1,), dtype=torch.int32, device=dev)
+    absmax = torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=dev)
     xs = torch.empty((1,), dtype=torch.float32, device=dev)
     xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
     y = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev)
@@ -204,7 +204,17 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     value = cnt["ops"] / (ms_per_step * 1e-3) / 1e12
-    conv_avg = float(conv_ms.mean())
+
+    # The dominant kernel's average launch duration: K back-to-back launches
+    # on the stream the kernel runs on, bracketed by two HIP events (per-launch
+    # event pairs above also include each launch's dispatch latency).
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(args.steps):
+        ops.causalconv3d_w8a8(xq, xs, wq, ws, b, cache, out=y)
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    conv_avg = cev[0].elapsed_time(cev[1]) / args.steps
     conv_tops = cnt["ops"] / (conv_avg * 1e-3) / 1e12
 
     # output sanity after the timed loop (no stale-output speedups)
@@ -251,7 +261,7 @@ def main():
         },
         "layer_ms": round(float(step_ms.mean()), 5),
         "conv_ms": round(conv_avg, 5),
-        "conv_ms_min": round(float(conv_ms.min()), 5),
+        "conv_ms_single_launch": round(float(conv_ms.mean()), 5),
         "conv_tops": round(conv_tops, 2),
         "nominal_ops": cnt["nominal_ops"],
         "quant_pass": {

@@ -81,30 +81,41 @@ int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh,
                           int kw, float clip_ratio, int8_t *wq,
                           float *w_scale, void *stream);
 
+/* Words of the activation-maximum buffer (see qvae_act_absmax). */
+#define QVAE_ABSMAX_WORDS 513
+
 /*
- * Dynamic activation absmax (scheme paragraph: dynamic symmetric INT8
- * activations; the scale is per tensor).
- *   x            bf16 bit patterns, numel elements (any layout)
- *   absmax_bits  uint32 [1] out: the bf16 bit pattern of max |x| (0..0x7F7F)
- * Inputs must be finite.  numel >= 1.
+ * Dynamic activation absmax, first of the two passes of the activation
+ * quantizer (scheme paragraph: dynamic symmetric INT8 activations; the scale
+ * is per tensor).
+ *   x       bf16 bit patterns, numel elements (any layout)
+ *   absmax  uint32 [QVAE_ABSMAX_WORDS], caller-allocated device buffer: this
+ *           pass writes per-workgroup partial maxima of |x| (as bf16 bit
+ *           patterns) into words 1.. ; qvae_act_quantize reduces them and
+ *           stores the bf16 bit pattern of max |x| (0..0x7F7F) in word 0.
+ * Inputs must be finite.  numel >= 1.  Pass the same x and numel to the
+ * following qvae_act_quantize.
  */
-int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax_bits,
+int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax,
                     void *stream);
 
 /*
- * Activation quantization with the scale derived on the device from
- * absmax_bits (fixed parameters: activation clip ratio 1.0).
- *   x_scale  float32 [1] out: s = fl(clip * absmax) / 127
+ * Activation quantization, second pass, with the scale derived on the device
+ * from the partial maxima of qvae_act_absmax (fixed parameters: activation
+ * clip ratio 1.0).
+ *   absmax   in: partial maxima; out: word 0 = bf16 bit pattern of max |x|
+ *   x_scale  float32 [1] out: s = fl(clip * max |x|) / 127
  *   xq       int8 [numel] out: clamp(rne(x / s), -127, 127), 0 when s == 0
  * Supported: clip_ratio == 1.0f.
  */
 int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
-                      const uint32_t *absmax_bits, float *x_scale, int8_t *xq,
+                      uint32_t *absmax, float *x_scale, int8_t *xq,
                       void *stream);
 
-/* qvae_act_absmax followed by qvae_act_quantize on the same stream. */
+/* qvae_act_absmax followed by qvae_act_quantize on the same stream (two
+ * launches, no host synchronization). */
 int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
-                          uint32_t *absmax_bits, float *x_scale, int8_t *xq,
+                          uint32_t *absmax, float *x_scale, int8_t *xq,
                           void *stream);
 
 /*

@@ -135,3 +135,9 @@ def test_product_never_reaches_the_oracle():
                 src = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), f
                 assert "qvae_oracle" not in src and "libqvae_oracle" not in src, f
+
+
+def test_absmax_words_match_header():
+    from w8a8_int8_quantized_act_amd import ops
+    m = re.search(r"#define\s+QVAE_ABSMAX_WORDS\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == ops.ABSMAX_WORDS

@@ -56,7 +56,7 @@ def _check_act(ops, x_bits):
     absmax_bits, x_scale, xq = ops.act_absmax_quant(xd)
     torch.cuda.synchronize()
     a, s, q = oracle.act_absmax_quant(x_bits)
-    assert int(absmax_bits.item()) == f32_bits(a) >> 16
+    assert int(absmax_bits[0].item()) == f32_bits(a) >> 16
     assert f32_bits(x_scale.item()) == f32_bits(s)
     got = xq.cpu().numpy()
     bad = np.count_nonzero(got != q)
@@ -93,6 +93,20 @@ def test_act_quant_near_ties(ops):
     a = torch.tensor([93.0])      # scale 93/127: quotients are near, not at, the ties
     x = torch.cat([a, base * (93.0 / 127.0)])
     _check_act(ops, _bits_of(x))
+
+
+def test_act_quant_split_entry_points(ops):
+    # the two passes called one by one (same buffers) give the combined call's result
+    g = torch.Generator().manual_seed(104)
+    xb = _bits_of(torch.randn(1_000_003, generator=g) * 2)
+    xd = to_dev_bits(xb)
+    absmax = ops.act_absmax(xd)
+    xs, xq = ops.act_quantize(xd, absmax)
+    torch.cuda.synchronize()
+    a, s, q = oracle.act_absmax_quant(xb)
+    assert int(absmax[0].item()) == f32_bits(a) >> 16
+    assert f32_bits(xs.item()) == f32_bits(s)
+    assert np.array_equal(xq.cpu().numpy(), q)
 
 
 def test_act_quant_zero_and_tiny(ops):
@@ -236,7 +250,7 @@ def _compare_full(ops, ci, r, n_random=1500, seed=0, cache_zero=False):
     assert np.array_equal(r["wq_d"].cpu().numpy(), pack_weight_codes(wq))
     assert np.array_equal(r["ws_d"].cpu().numpy().view(np.uint32), ws.view(np.uint32))
     a, s, xq = oracle.act_absmax_quant(ci.x)
-    assert int(r["absmax"].item()) == f32_bits(a) >> 16
+    assert int(r["absmax"][0].item()) == f32_bits(a) >> 16
     assert f32_bits(r["xs"].item()) == f32_bits(s)
     got_xq = r["xq_d"].cpu().numpy()
     assert np.array_equal(got_xq, xq), f"{np.count_nonzero(got_xq != xq)} codes differ"

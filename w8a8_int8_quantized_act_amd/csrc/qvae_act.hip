@@ -7,15 +7,19 @@
 //
 // Two HBM-bound passes.  The scale is a grid-wide dependency, so the max is
 // reduced first (pass 1) and every quantize workgroup derives the same scale
-// from the reduced word (pass 2); the scale never visits the host.
+// from the reduced maxima (pass 2); the scale never visits the host.
 //
 //   pass 1  k_absmax    16-byte loads of bf16, integer max of |x| bit patterns
 //                       (for finite bf16, |a| < |b| iff (a & 0x7FFF) <
 //                       (b & 0x7FFF) as integers), packed 2x16-bit max, DPP
-//                       wave reduction, LDS workgroup reduction, one atomicMax
-//                       per workgroup into the output word (cleared first by a
-//                       one-lane kernel on the same stream).
-//   pass 2  k_quantize  32 bytes of bf16 in, 16 int8 codes out per lane.
+//                       wave reduction, LDS workgroup reduction; each
+//                       workgroup writes its own partial maximum (no atomics:
+//                       hundreds of same-address atomics serialize in L2 and
+//                       cost more than the whole pass).
+//   pass 2  k_quantize  every workgroup reduces the <= 512 partials (2 KB from
+//                       L2), derives s, and quantizes: 32 bytes of bf16 in,
+//                       16 int8 codes out per lane.  Workgroup 0 publishes the
+//                       maximum and the scale.
 //
 // The quotient x / s is the IEEE binary32 one.  The kernel computes t = x * r
 // with r = fl(1 / s) and keeps rne(t) when t is far from a rounding boundary:
@@ -30,8 +34,6 @@ namespace qvae {
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(64) void k_absmax_clear(uint32_t *word) { *word = 0u; }
-
 // Packed 2x16-bit unsigned max of the magnitudes held in one 32-bit word.
 __device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
 {
@@ -40,14 +42,34 @@ __device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
-constexpr int kAbsmaxThreads = 256;
+constexpr int kAbsmaxThreads = 1024;
 constexpr int kAbsmaxUnroll = 4;   // 16-byte loads in flight per lane
+constexpr int kAbsmaxParts = QVAE_ABSMAX_WORDS - 1;
 
-__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restrict__ x16,
-                                                          int64_t n16,
-                                                          const uint16_t *__restrict__ tail,
-                                                          int ntail,
-                                                          uint32_t *__restrict__ out)
+// Number of workgroups (= partial maxima) of the absmax pass for numel.
+static int absmax_blocks(int64_t numel)
+{
+    const int64_t n16 = numel / 8;
+    int64_t want = (n16 + (int64_t)kAbsmaxThreads * kAbsmaxUnroll - 1) / ((int64_t)kAbsmaxThreads * kAbsmaxUnroll);
+    if (want < 1) want = 1;
+    if (want > kAbsmaxParts) want = kAbsmaxParts;
+    return (int)want;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *part /* [blockDim/64] LDS */)
+{
+    m = wave_max_u32(m);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) part[wave] = m;
+    __syncthreads();
+    uint32_t b = part[0];
+    for (int k = 1; k < (int)(blockDim.x >> 6); ++k) b = max(b, part[k]);
+    return b;
+}
+
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restrict__ x16, int64_t n16,
+                                                          const uint16_t *__restrict__ tail, int ntail,
+                                                          uint32_t *__restrict__ partials)
 {
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * kAbsmaxThreads;
@@ -73,18 +95,9 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
     }
     if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = pk_absmax(m, tail[threadIdx.x]);
     m = max(m & 0xFFFFu, m >> 16);
-    m = wave_max_u32(m);
-
     __shared__ uint32_t part[kAbsmaxThreads / 64];
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) part[wave] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t b = part[0];
-#pragma unroll
-        for (int k = 1; k < kAbsmaxThreads / 64; ++k) b = max(b, part[k]);
-        atomicMax(out, b);
-    }
+    const uint32_t b = block_max_u32(m, part);
+    if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
 // One activation code: clamp(rne(x / s), -127, 127).
@@ -120,17 +133,26 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
                                                            const uint16_t *__restrict__ x,
                                                            int64_t numel,
                                                            float clip_ratio,
-                                                           const uint32_t *__restrict__ absmax_bits,
+                                                           uint32_t *__restrict__ absmax,
+                                                           int nparts,
                                                            float *__restrict__ x_scale,
                                                            u32x4 *__restrict__ q16,
                                                            int8_t *__restrict__ q)
 {
-    const float a = bf16_bits_to_float(*absmax_bits);
+    // the tensor's maximum from the absmax pass's partial maxima
+    uint32_t mp = 0;
+    for (int k = threadIdx.x; k < nparts; k += kQuantThreads) mp = max(mp, absmax[1 + k]);
+    __shared__ uint32_t part[kQuantThreads / 64];
+    const uint32_t mbits = block_max_u32(mp, part);
+    const float a = bf16_bits_to_float(mbits);
     const float s = (clip_ratio * a) / 127.0f;
     const float r = 1.0f / s;
     const bool zero = !(s > 0.0f);
     const bool exact_only = !(r < __builtin_inff());
-    if (blockIdx.x == 0 && threadIdx.x == 0) *x_scale = s;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        absmax[0] = mbits;
+        *x_scale = s;
+    }
 
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
     for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n32; i += stride) {
@@ -160,49 +182,43 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
 
 using namespace qvae;
 
-extern "C" int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax_bits, void *stream)
+extern "C" int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax, void *stream)
 {
     if (force_fail()) return QVAE_EFORCED;
-    if (!x || !absmax_bits || numel <= 0) return QVAE_EINVAL;
+    if (!x || !absmax || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x)) return QVAE_EINVAL;
-    hipStream_t st = as_stream(stream);
     const int64_t n16 = numel / 8;
     const int ntail = (int)(numel - n16 * 8);
-    int64_t want = (n16 + (int64_t)kAbsmaxThreads * kAbsmaxUnroll - 1) / ((int64_t)kAbsmaxThreads * kAbsmaxUnroll);
-    int64_t cap = (int64_t)device_cus() * 8;
-    int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-    hipLaunchKernelGGL(k_absmax_clear, dim3(1), dim3(64), 0, st, absmax_bits);
-    hipLaunchKernelGGL(k_absmax, dim3(blocks), dim3(kAbsmaxThreads), 0, st,
-                       reinterpret_cast<const u32x4 *>(x), n16, x + n16 * 8, ntail, absmax_bits);
+    hipLaunchKernelGGL(k_absmax, dim3(absmax_blocks(numel)), dim3(kAbsmaxThreads), 0, as_stream(stream),
+                       reinterpret_cast<const u32x4 *>(x), n16, x + n16 * 8, ntail, absmax + 1);
     return launch_status();
 }
 
-extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
-                                 const uint32_t *absmax_bits, float *x_scale, int8_t *xq, void *stream)
+extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio, uint32_t *absmax,
+                                 float *x_scale, int8_t *xq, void *stream)
 {
     if (force_fail()) return QVAE_EFORCED;
-    if (!x || !absmax_bits || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
+    if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
     if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
-    hipStream_t st = as_stream(stream);
     const int64_t n32 = numel / 16;
     int64_t want = (n32 + kQuantThreads - 1) / kQuantThreads;
     int64_t cap = (int64_t)device_cus() * 16;
     int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-    hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, st,
-                       reinterpret_cast<const u32x4 *>(x), n32, x, numel, clip_ratio, absmax_bits,
+    hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, as_stream(stream),
+                       reinterpret_cast<const u32x4 *>(x), n32, x, numel, clip_ratio, absmax, absmax_blocks(numel),
                        x_scale, reinterpret_cast<u32x4 *>(xq), xq);
     return launch_status();
 }
 
-extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
-                                     uint32_t *absmax_bits, float *x_scale, int8_t *xq, void *stream)
+extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio, uint32_t *absmax,
+                                     float *x_scale, int8_t *xq, void *stream)
 {
     if (force_fail()) return QVAE_EFORCED;
-    if (!x || !absmax_bits || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
+    if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
     if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
-    int rc = qvae_act_absmax(x, numel, absmax_bits, stream);
+    int rc = qvae_act_absmax(x, numel, absmax, stream);
     if (rc != QVAE_OK) return rc;
-    return qvae_act_quantize(x, numel, clip_ratio, absmax_bits, x_scale, xq, stream);
+    return qvae_act_quantize(x, numel, clip_ratio, absmax, x_scale, xq, stream);
 }

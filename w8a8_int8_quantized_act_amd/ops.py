@@ -26,6 +26,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqvae.so")
 
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EFORCED = 0, -1, -2, -3, -4
+ABSMAX_WORDS = 513   # QVAE_ABSMAX_WORDS: word 0 = bf16 bits of max|x|, then partial maxima
 
 
 class QvaeError(RuntimeError):
@@ -123,10 +124,11 @@ def _bits_view(x: torch.Tensor):
 
 
 def act_absmax(x: torch.Tensor, absmax_bits: torch.Tensor | None = None, stream=None):
-    """-> int32 [1] device tensor holding the bf16 bit pattern of max |x|."""
+    """First activation pass: partial maxima into the int32 [ABSMAX_WORDS] buffer
+    (word 0 is filled in by act_quantize)."""
     _dev(_bits_view(x), "x")
     if absmax_bits is None:
-        absmax_bits = torch.empty((1,), dtype=torch.int32, device=x.device)
+        absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=x.device)
     _check(lib().qvae_act_absmax(_p(x), x.numel(), _p(absmax_bits), _stream(stream)), "qvae_act_absmax")
     return absmax_bits
 
@@ -146,11 +148,12 @@ def act_quantize(x: torch.Tensor, absmax_bits: torch.Tensor, clip_ratio: float =
 
 def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None, x_scale=None, xq=None,
                      stream=None):
-    """-> (absmax_bits int32 [1], x_scale float32 [1], xq int8 of x's shape)."""
+    """-> (absmax_bits int32 [ABSMAX_WORDS] (word 0 = bf16 bits of max|x|), x_scale float32 [1],
+    xq int8 of x's shape)."""
     _dev(_bits_view(x), "x")
     dev = x.device
     if absmax_bits is None:
-        absmax_bits = torch.empty((1,), dtype=torch.int32, device=dev)
+        absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=dev)
     if x_scale is None:
         x_scale = torch.empty((1,), dtype=torch.float32, device=dev)
     if xq is None:
