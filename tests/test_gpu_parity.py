@@ -338,3 +338,32 @@ def test_workload_video_chunked(ops):
     assert ulp_dist(bf16_bits(chunked.reshape(-1, spec.Cout)[pos_d]), ref_y).max() == 0
     ref_p = oracle.epilogue(oracle.conv_acc(xq, wp, None, positions=pos), s, wps, ci.b_proj)
     assert ulp_dist(bf16_bits(proj.reshape(-1, spec.proj_cout)[pos_d]), ref_p).max() == 0
+
+
+def test_layer_step_in_hip_graph(ops):
+    # absmax -> quantize -> conv captured once and replayed several times, with
+    # the program's own eager work in between; every replay equals the eager result
+    ci = wl.draw_custom(370, 1, 192, 192, 2, 21, 35, x_kind="silu")
+    x = to_dev_bits(ci.x)
+    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    b = torch.from_numpy(ci.b).to(DEV)
+    absmax = torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=DEV)
+    xs = torch.empty((1,), dtype=torch.float32, device=DEV)
+    xq = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    y = torch.empty((1, 2, 21, 35, 192), dtype=torch.bfloat16, device=DEV)
+    y_eager, xs_eager, _ = ops.layer_forward(x, wq, ws, b)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.act_absmax_quant(x, absmax_bits=absmax, x_scale=xs, xq=xq)
+        ops.causalconv3d_w8a8(xq, xs, wq, ws, b, out=y)
+    for rep in range(4):
+        y.zero_()
+        xs.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), f"replay {rep}"
+        assert xs.item() == xs_eager.item()
+        other = ops.causalconv3d_w8a8(xq, xs, wq, ws, None)      # eager work between replays
+        torch.cuda.synchronize()
+        del other
