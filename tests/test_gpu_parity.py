@@ -354,8 +354,9 @@ def test_layer_step_in_hip_graph(ops):
     y_eager, xs_eager, _ = ops.layer_forward(x, wq, ws, b)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        ops.act_absmax_quant(x, absmax_bits=absmax, x_scale=xs, xq=xq)
+    with torch.cuda.graph(g):               # the two separate passes (cooperative launches are not captured)
+        ops.act_absmax(x, absmax_bits=absmax)
+        ops.act_quantize(x, absmax, x_scale=xs, xq=xq)
         ops.causalconv3d_w8a8(xq, xs, wq, ws, b, out=y)
     for rep in range(4):
         y.zero_()

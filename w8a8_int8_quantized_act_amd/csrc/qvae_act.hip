@@ -49,8 +49,9 @@ constexpr int kAbsmaxParts = QVAE_ABSMAX_WORDS - 1;
 // Number of workgroups (= partial maxima) of the absmax pass for numel.
 static int absmax_blocks(int64_t numel)
 {
+    // at least one 16-byte vector per lane, all CUs busy for mid-sized tensors
     const int64_t n16 = numel / 8;
-    int64_t want = (n16 + (int64_t)kAbsmaxThreads * kAbsmaxUnroll - 1) / ((int64_t)kAbsmaxThreads * kAbsmaxUnroll);
+    int64_t want = (n16 + kAbsmaxThreads - 1) / kAbsmaxThreads;
     if (want < 1) want = 1;
     if (want > kAbsmaxParts) want = kAbsmaxParts;
     return (int)want;

@@ -376,31 +376,23 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     typedef float f4 __attribute__((ext_vector_type(4)));
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    f4 fm[MB][4], fb[MB][4];
-    if constexpr (!ACC32) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
-                fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
-                fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
-            }
-    }
     auto finish_block = [&](int nb, const v16i (&accb)[MB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
+                const int col = mb * 32 + g * 8 + lhalf * 4;   // channel offset within the wave
+                char *dst = stage + lrow * EPITCH + col * ELEM;
                 if constexpr (ACC32) {
                     *reinterpret_cast<v4i *>(dst) =
                         v4i{accb[mb][4 * g], accb[mb][4 * g + 1], accb[mb][4 * g + 2], accb[mb][4 * g + 3]};
                 } else {
+                    // per-channel factors and biases of this lane's four channels (LDS)
+                    const f4 fm = *reinterpret_cast<const f4 *>(s_fac + wco * MB * 32 + col);
+                    const f4 fb = *reinterpret_cast<const f4 *>(s_fac + C::BCO + wco * MB * 32 + col);
                     f4 y;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[e] = __builtin_fmaf((float)accb[mb][4 * g + e], fm[mb][g][e], fb[mb][g][e]);
+                    for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf((float)accb[mb][4 * g + e], fm[e], fb[e]);
                     const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
                     const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
                     *reinterpret_cast<uint2 *>(dst) =
@@ -488,8 +480,10 @@ static int launch_spatial(const ConvArgs &a, bool acc32, hipStream_t st)
             return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
         if (a.Cout % 192 == 0) return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
         if constexpr (KH * KW > 1) {
-            if (px_tiles(a, 16, 32) * (a.Cout / 96) >= cus || !k2)
-                return launch_cfg<1, 4, 1, 3, 4, 16, 32, KH, KW, SPW>(a, acc32, st);
+            // 96 channels: memory-bound; 96x64 wave tiles keep two workgroups
+            // per CU so one's loads and stores overlap the other's MFMAs
+            if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
+                return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, acc32, st);
         } else {
             if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
                 return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
