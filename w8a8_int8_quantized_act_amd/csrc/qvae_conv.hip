@@ -88,6 +88,10 @@ struct ConvCfg {
     // one 32-channel slice of the halo; slices are 32 bytes apart modulo 128
     // so the chunks of one pixel written by consecutive lanes spread over banks
     static constexpr int SLICE_BYTES = (HH * HWD * kHaloPitch + 127) / 128 * 128 + 32;
+    // the padding after slice 0's pixels, never read: the halo stores of lanes
+    // without a chunk go there so the store loop needs no branch
+    static constexpr int HALO_PAD = HH * HWD * kHaloPitch;
+    static_assert(HALO_PAD + 16 <= SLICE_BYTES, "padding holds one 16-byte chunk");
     static constexpr int BUF_BYTES = SL * SLICE_BYTES;
     static constexpr int HALO_CHUNKS = SL * HH * HWD * 2;
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
@@ -139,20 +143,24 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     // ---- halo load descriptors (stage independent parts).  Chunk u covers
     // pixel q = u / (2*SL) and 16 bytes c = u % (2*SL) of its SL slices, so
     // consecutive lanes read each pixel's 32*SL contiguous bytes together.
-    int h_off[C::HALO_PT];   // byte offset in a frame, -1 = outside the image
-    int h_lds[C::HALO_PT];   // LDS byte offset inside a stage buffer, -1 = idle lane
+    // The loads are raw buffer loads: a pixel outside the image gets an
+    // offset past the buffer's size, and the hardware returns zeros for it,
+    // so neither the loads nor the LDS stores branch per lane.
+    constexpr uint32_t kOutside = 0x80000000u;   // >= any frame size (frames are < 2^31 bytes)
+    uint32_t h_off[C::HALO_PT];   // byte offset from the stage's slice base, kOutside = zero pixel
+    int h_lds[C::HALO_PT];        // LDS byte offset inside a stage buffer (idle lanes: slice padding)
 #pragma unroll
     for (int k = 0; k < C::HALO_PT; ++k) {
         const int u = tid + k * NT;
-        h_off[k] = -1;
-        h_lds[k] = -1;
+        h_off[k] = kOutside;
+        h_lds[k] = C::HALO_PAD;
         if (u < C::HALO_CHUNKS) {
             const int q = u / (2 * C::SL), c = u - q * (2 * C::SL);
             const int sl = c >> 1, half = c & 1;
             const int hh = q / C::HWD, ww = q - hh * C::HWD;
             const int gh = h0 - PH + hh, gw = w0 - PW + ww;
             h_lds[k] = sl * C::SLICE_BYTES + q * kHaloPitch + half * 16;
-            if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (gh * W + gw) * Cin + c * 16;
+            if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (uint32_t)((gh * W + gw) * Cin + c * 16);
         }
     }
     const size_t frame_bytes = (size_t)H * W * Cin;
@@ -162,22 +170,27 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         return a.cache + ((size_t)n * (kt - 1) + (kt - 1 + tau)) * frame_bytes;
     };
     v4i hreg[C::HALO_PT];
-    auto load_halo = [&](int st) {
+    auto halo_rsrc = [&](int st) {
         const int it = st / nsp;
         const int p = st - it * nsp;
-        const int8_t *fp = frame_ptr(i_lo + it);
-        const int8_t *fps = fp + p * C::SL * 32;
+        const int8_t *fps = frame_ptr(i_lo + it) + p * C::SL * 32;
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(fps), 0,
+                                                 (int)(frame_bytes - (size_t)p * C::SL * 32), 0x00020000);
+    };
+    auto load_chunk = [&](__amdgpu_buffer_rsrc_t rs, int k) {
+        hreg[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)h_off[k], 0, 0));
+    };
+    auto store_chunk = [&](int buf, int k) {
+        *reinterpret_cast<v4i *>(smem + buf * C::BUF_BYTES + h_lds[k]) = hreg[k];
+    };
+    auto load_halo = [&](int st) {
+        const __amdgpu_buffer_rsrc_t rs = halo_rsrc(st);
 #pragma unroll
-        for (int k = 0; k < C::HALO_PT; ++k) {
-            hreg[k] = v4i{0, 0, 0, 0};
-            if (h_off[k] >= 0) hreg[k] = *reinterpret_cast<const v4i *>(fps + h_off[k]);
-        }
+        for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rs, k);
     };
     auto store_halo = [&](int buf) {
-        char *xs = smem + buf * C::BUF_BYTES;
 #pragma unroll
-        for (int k = 0; k < C::HALO_PT; ++k)
-            if (h_lds[k] >= 0) *reinterpret_cast<v4i *>(xs + h_lds[k]) = hreg[k];
+        for (int k = 0; k < C::HALO_PT; ++k) store_chunk(buf, k);
     };
 
     // ---- wave roles (wave-uniform: keep them in scalar registers so every
@@ -259,6 +272,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     lds_barrier();
 
     // B fragments of k-step e of the stage held in buffer xs
+    auto read_b1 = [&](const char *xs, int e, int nb) -> v4i {
+        const int sp = e / C::KHW, tap = e % C::KHW;
+        const int j = tap / KW, l = tap % KW;
+        return *reinterpret_cast<const v4i *>(xs + sp * C::SLICE_BYTES + (j * C::HWD + l) * kHaloPitch + b_q0[nb]);
+    };
     auto read_b = [&](const char *xs, int e, v4i (&bv)[NB]) {
         const int sp = e / C::KHW, tap = e % C::KHW;
         const int j = tap / KW, l = tap % KW;
@@ -273,35 +291,69 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         // the next stage's weights (the current ones again after the last
         // stage: harmless reads, no branch in the loop body)
         const int8_t *wnext = wstage(more ? st + 1 : st);
-        if (more) load_halo(st + 1);
+        // The next stage's halo (the current one again after the last stage:
+        // in-bounds reads into a buffer nobody reads any more).  When the
+        // stage has enough k-steps, chunk k is loaded in step k and stored to
+        // the other buffer in step k + PD, one instruction per step between
+        // two MFMAs; otherwise all chunks are loaded here and stored in one
+        // step.
+        constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
+        const __amdgpu_buffer_rsrc_t rsn = halo_rsrc(more ? st + 1 : st);
+        if constexpr (!SPREAD) {
+            if (more) {
+#pragma unroll
+                for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
+            }
+        }
         const char *xs = smem + buf * C::BUF_BYTES;
         v4i bcur[NB], bnext[NB];
         read_b(xs, 0, bcur);
-        // Each k-step: LDS reads of the next step's B fragments (issued first,
-        // so they land while this step's MFMAs run), the MB x NB MFMAs of this
-        // step, then the weight loads PD steps ahead into the ring slot just
-        // consumed.  The scheduling barriers keep every load in the step it
-        // was issued in (the scheduler would otherwise sink the prefetches
-        // down to their use and expose the L2 latency).
+        // Each k-step issues its MB x NB MFMAs with one memory instruction
+        // after each of the first few: the LDS read of the next step's B
+        // fragment nb after MFMA nb, and the reload of weight ring slot row
+        // mb (PD steps ahead) right after the last MFMA that reads it.  A
+        // wave has one MFMA in flight at a time, so a memory instruction
+        // issued between two MFMAs costs nothing, while a cluster of them
+        // stalls the matrix pipe.  The scheduling barriers pin this order (the
+        // scheduler would otherwise sink the prefetches down to their use
+        // and expose their latency).
 #pragma unroll
         for (int e = 0; e < C::KS; ++e) {
             const int slot = e % C::PD;
-            if (e + 1 < C::KS) read_b(xs, e + 1, bnext);
-            __builtin_amdgcn_sched_barrier(0);
+            const int8_t *wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024
+                                                     : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
+                for (int nb = 0; nb < NB; ++nb) {
+                    constexpr int last = MB * NB - 1;
+                    const int i = mb * NB + nb;
                     acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
-            if (e + C::PD < C::KS)
-                load_w(wcur + (e + C::PD) * 1024, slot);
-            else
-                load_w(wnext + (e + C::PD - C::KS) * 1024, slot);
-            // The next stage's halo goes to the other buffer as soon as its
-            // loads are covered by a wait this step needs anyway (they were
-            // issued before the weights of step PD); nobody reads that buffer
-            // after the previous stage's barrier.
-            if (e == C::HALO_STORE_STEP && more) store_halo(buf ^ 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (i < NB && e + 1 < C::KS) bnext[i] = read_b1(xs, e + 1, i);
+#pragma unroll
+                    for (int m2 = 0; m2 < MB; ++m2) {
+                        const int at = (m2 == 0) ? (NB < last ? NB : last) : (m2 + 1) * NB - 1;
+                        if (i == at) wreg[slot][m2] = *reinterpret_cast<const v4i *>(wsrc + m2 * cb_stride);
+                    }
+                    if constexpr (SPREAD) {
+                        // halo chunk e goes out right after weight row 0, so
+                        // the wait for weight row 1 of the same step (PD steps
+                        // later) covers it and its store needs no extra wait
+                        constexpr int hl = NB < last ? NB : last;
+                        constexpr int hs = NB + 1 < last ? NB + 1 : last;
+                        if (i == hl && e < C::HALO_PT) load_chunk(rsn, e);
+                        if (i == hs && e >= C::PD && e - C::PD < C::HALO_PT) store_chunk(buf ^ 1, e - C::PD);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            // Without spreading, the next stage's halo goes to the other buffer
+            // as soon as its loads are covered by a wait this step needs anyway
+            // (they were issued before the weights of step PD); nobody reads
+            // that buffer after the previous stage's barrier.
+            if constexpr (!SPREAD) {
+                if (e == C::HALO_STORE_STEP && more) store_halo(buf ^ 1);
+            }
             __builtin_amdgcn_sched_barrier(0);
             if (e + 1 < C::KS) {
 #pragma unroll
