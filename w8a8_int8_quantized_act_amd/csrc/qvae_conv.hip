@@ -50,6 +50,7 @@ namespace qvae {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 struct ConvArgs {
     const int8_t *xq;
@@ -365,13 +366,16 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     }
 
     // ---- split K: each half finishes half of the pixel blocks.  Wave wk
-    // exports to LDS the blocks the other half finishes, then adds the
-    // other half's export of its own blocks (INT32 sums, exact in any order).
+    // exports to LDS the blocks the other half finishes; after the barrier it
+    // reads the other half's export of its own blocks into registers and adds
+    // it while rescaling (INT32 sums, exact in any order).
+    constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
+    v4i part[(WK > 1) ? MB * HB * 4 : 1];
     if constexpr (WK > 1) {
-        constexpr int HB = NB / 2;
-        auto xchg = [&](auto wkc) {
-            constexpr int me = decltype(wkc)::value, other = 1 - me;
-            int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + me) * C::XB);
+        int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
+        const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
+        auto xport = [&](auto wkc) {
+            constexpr int other = 1 - decltype(wkc)::value;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -382,26 +386,17 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                         exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
                             make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
                     }
-            __syncthreads();
-            const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + other) * C::XB);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int j = 0; j < HB; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const int4 u = exp_other[((mb * HB + j) * 4 + g) * 64 + lane];
-                        v16i &v = acc[mb][me * HB + j];
-                        v[4 * g] += u.x;
-                        v[4 * g + 1] += u.y;
-                        v[4 * g + 2] += u.z;
-                        v[4 * g + 3] += u.w;
-                    }
         };
         if (wk == 0)
-            xchg(std::integral_constant<int, 0>{});
+            xport(std::integral_constant<int, 0>{});
         else
-            xchg(std::integral_constant<int, 1>{});
+            xport(std::integral_constant<int, 1>{});
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < MB * HB * 4; ++q) {
+            const int4 u = exp_other[q * 64 + lane];
+            part[q] = v4i{u.x, u.y, u.z, u.w};
+        }
     }
 
     // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
@@ -411,7 +406,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     // packed convert), written to the wave's LDS staging rows
     // [pixel][channel], then read back row-wise so every lane stores 16
     // contiguous bytes and consecutive lanes continue along the channels-last
-    // output row.
+    // output row.  The stores are raw buffer stores relative to the tile's
+    // first output: a pixel outside the image gets an offset past the
+    // buffer's size and the hardware drops it, so no lane branches.
     constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
     constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
     constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
@@ -420,31 +417,58 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     static_assert(32 * EPITCH <= C::EPI_WAVE_BYTES, "staging rows fit the wave's LDS slice");
     static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
     // staging: with split K the partner's export slice (this wave has read it
-    // and nobody else touches it); otherwise a slice per wave
+    // into registers and nobody else touches it); otherwise a slice per wave
     char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : wr * C::EPI_WAVE_BYTES);
 
-    const size_t pix_base = ((size_t)n * a.T + t) * H;
     const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
+    const size_t tile_first = ((((size_t)n * a.T + t) * H + h0) * W + w0) * (size_t)a.Cout + cw0;
+    const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
+    const size_t left = (out_total - tile_first) * ELEM;
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
+    const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
     typedef float f4 __attribute__((ext_vector_type(4)));
     typedef float f2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    auto finish_block = [&](int nb, const v16i (&accb)[MB]) {
+    // this lane's per-channel factors and biases: read from LDS once when the
+    // wave tile is large (one wave per SIMD anyway, registers to spare after
+    // the K loop), else at each use so small tiles keep two waves per SIMD
+    constexpr bool HOIST = !ACC32 && MB * NB >= 12;
+    f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
+    if constexpr (HOIST) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int col = mb * 32 + g * 8 + lhalf * 4;   // channel offset within the wave
-                char *dst = stage + lrow * EPITCH + col * ELEM;
+                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
+                fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
+                fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
+            }
+    }
+    // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
+    auto finish_block = [&](auto wkc, int j) {
+        constexpr int WKC = decltype(wkc)::value;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const v16i &x = acc[mb][WKC * HB + j];
+                v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
                 if constexpr (ACC32) {
-                    *reinterpret_cast<v4i *>(dst) =
-                        v4i{accb[mb][4 * g], accb[mb][4 * g + 1], accb[mb][4 * g + 2], accb[mb][4 * g + 3]};
+                    *reinterpret_cast<v4i *>(dst) = v;
                 } else {
-                    // per-channel factors and biases of this lane's four channels (LDS)
-                    const f4 fm = *reinterpret_cast<const f4 *>(s_fac + wco * MB * 32 + col);
-                    const f4 fb = *reinterpret_cast<const f4 *>(s_fac + C::BCO + wco * MB * 32 + col);
                     f4 y;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) y[e] = __builtin_fmaf((float)accb[mb][4 * g + e], fm[e], fb[e]);
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (HOIST) {
+                            y[e] = __builtin_fmaf((float)v[e], fm[mb][g][e], fb[mb][g][e]);
+                        } else {
+                            const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
+                            y[e] = __builtin_fmaf((float)v[e], s_fac[col], s_fac[C::BCO + col]);
+                        }
+                    }
                     const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
                     const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
                     *reinterpret_cast<uint2 *>(dst) =
@@ -457,34 +481,21 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
             const int px = c / (ROWB / 16);
             const int off = (c - px * (ROWB / 16)) * 16;
             const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
-            const int p = (wpx * NB + nb) * 32 + px;
+            const int p = (wpx * NB + WKC * HB + j) * 32 + px;
             const int pr = p / TW, pc = p - pr * TW;
-            const int gh = h0 + pr, gw = w0 + pc;
-            if (gh < H && gw < W) {
-                char *o = static_cast<char *>(a.out) +
-                          (((pix_base + gh) * W + gw) * (size_t)a.Cout + cw0) * ELEM + off;
-                *reinterpret_cast<v4i *>(o) = v;
-            }
+            const bool inside = h0 + pr < H && w0 + pc < W;
+            const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, 0);
         }
     };
-    auto finish_range = [&](auto lo_c, auto hi_c) {
-        constexpr int lo = decltype(lo_c)::value, hi = decltype(hi_c)::value;
+    auto finish_all = [&](auto wkc) {
 #pragma unroll
-        for (int nb = lo; nb < hi; ++nb) {
-            v16i accb[MB];
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) accb[mb] = acc[mb][nb];
-            finish_block(nb, accb);
-        }
+        for (int j = 0; j < HB; ++j) finish_block(wkc, j);
     };
-    if constexpr (WK > 1) {
-        if (wk == 0)
-            finish_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NB / 2>{});
-        else
-            finish_range(std::integral_constant<int, NB / 2>{}, std::integral_constant<int, NB>{});
-    } else {
-        finish_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NB>{});
-    }
+    if (WK > 1 && wk == 1)
+        finish_all(std::integral_constant<int, 1>{});
+    else
+        finish_all(std::integral_constant<int, 0>{});
 }
 
 // ---- host side ------------------------------------------------------------
@@ -560,6 +571,8 @@ static int conv_validate(const int8_t *xq, const int8_t *wq, const void *out, in
     if (K * 127 * 127 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
     // byte offsets inside one frame are 32-bit
     if ((int64_t)H * W * Cin >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
+    // output byte offsets inside one pixel tile (at most 32 rows, INT32 export) are 32-bit
+    if ((int64_t)32 * W * Cout * 4 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
     return QVAE_OK;
 }
 
