@@ -208,18 +208,23 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     // ((((cb * kt + i) * S + s) * KHW + tap) * 64 + lane) * 16.  Within one
     // stage a wave walks KS consecutive fragments, so the k-step e of stage st
     // is at wstage(st) + e * 1 KB.
-    const size_t cb_stride = (size_t)kt * S * C::KHW * 1024;
-    const int8_t *wbase = a.wq + (size_t)(co0 / 32 + wco * MB) * cb_stride + lane * 16;
-    auto wstage = [&](int st) -> const int8_t * {
+    // The loads are raw buffer loads from this wave's weight slab: the
+    // offset of a fragment is wave-uniform (a scalar operand) and the lane's
+    // 16 bytes are a constant vector offset, so a load needs no address
+    // arithmetic.
+    const int cb_stride = kt * S * C::KHW * 1024;          // bytes per 32-channel block (< 2^23)
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
+    const int wlane = lane * 16;
+    auto wstage = [&](int st) -> int {
         const int it = st / nsp;
         const int p = st - it * nsp;
-        return wbase + (size_t)(((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
+        return (((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
+    };
+    auto load_wf = [&](int off) -> v4i {
+        return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off, 0));
     };
     v4i wreg[C::PD][MB];
-    auto load_w = [&](const int8_t *src, int slot) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) wreg[slot][mb] = *reinterpret_cast<const v4i *>(src + mb * cb_stride);
-    };
 
     // B fragment base offsets (pixel of lane, within the stage buffer)
     int b_q0[NB];
@@ -255,9 +260,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         }
     }
 
-    const int8_t *wcur = wstage(0);
+    int wcur = wstage(0);
 #pragma unroll
-    for (int e = 0; e < C::PD; ++e) load_w(wcur + e * 1024, e);
+    for (int e = 0; e < C::PD; ++e)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
     load_halo(0);
     store_halo(0);
     if constexpr (!ACC32) {
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         const bool more = st + 1 < nst;
         // the next stage's weights (the current ones again after the last
         // stage: harmless reads, no branch in the loop body)
-        const int8_t *wnext = wstage(more ? st + 1 : st);
+        const int wnext = wstage(more ? st + 1 : st);
         // The next stage's halo (the current one again after the last stage:
         // in-bounds reads into a buffer nobody reads any more).  When the
         // stage has enough k-steps, chunk k is loaded in step k and stored to
@@ -321,8 +328,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int e = 0; e < C::KS; ++e) {
             const int slot = e % C::PD;
-            const int8_t *wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024
-                                                     : wnext + (e + C::PD - C::KS) * 1024;
+            const int wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024 : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
                     for (int m2 = 0; m2 < MB; ++m2) {
                         const int at = (m2 == 0) ? (NB < last ? NB : last) : (m2 + 1) * NB - 1;
-                        if (i == at) wreg[slot][m2] = *reinterpret_cast<const v4i *>(wsrc + m2 * cb_stride);
+                        if (i == at) wreg[slot][m2] = load_wf(wsrc + m2 * cb_stride);
                     }
                     if constexpr (SPREAD) {
                         // halo chunk e goes out right after weight row 0, so
