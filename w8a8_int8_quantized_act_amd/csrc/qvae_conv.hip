@@ -293,25 +293,23 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
     };
 
-    for (int st = 0; st < nst; ++st) {
+    // One stage.  MORE = a next stage exists: then its weights enter the ring
+    // in the last PD k-steps and its halo goes to the other buffer.  The last
+    // stage is a separate instantiation without those loads, so the epilogue
+    // never waits for prefetches nobody uses.
+    constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
+    auto run_stage = [&](int st, auto more_c) {
+        constexpr bool MORE = decltype(more_c)::value;
         const int buf = st & 1;
-        const bool more = st + 1 < nst;
-        // the next stage's weights (the current ones again after the last
-        // stage: harmless reads, no branch in the loop body)
-        const int wnext = wstage(more ? st + 1 : st);
-        // The next stage's halo (the current one again after the last stage:
-        // in-bounds reads into a buffer nobody reads any more).  When the
-        // stage has enough k-steps, chunk k is loaded in step k and stored to
-        // the other buffer in step k + PD, one instruction per step between
-        // two MFMAs; otherwise all chunks are loaded here and stored in one
-        // step.
-        constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
-        const __amdgpu_buffer_rsrc_t rsn = halo_rsrc(more ? st + 1 : st);
-        if constexpr (!SPREAD) {
-            if (more) {
+        const int wnext = MORE ? wstage(st + 1) : wcur;
+        // When the stage has enough k-steps, halo chunk k of the next stage is
+        // loaded in step k and stored to the other buffer in step k + PD, one
+        // instruction per step between two MFMAs; otherwise all chunks are
+        // loaded here and stored in one step.
+        const __amdgpu_buffer_rsrc_t rsn = halo_rsrc(MORE ? st + 1 : st);
+        if constexpr (!SPREAD && MORE) {
 #pragma unroll
-                for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
-            }
+            for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
         }
         const char *xs = smem + buf * C::BUF_BYTES;
         v4i bcur[NB], bnext[NB];
@@ -328,6 +326,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int e = 0; e < C::KS; ++e) {
             const int slot = e % C::PD;
+            const bool wload = e + C::PD < C::KS || MORE;
             const int wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024 : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -341,9 +340,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
                     for (int m2 = 0; m2 < MB; ++m2) {
                         const int at = (m2 == 0) ? (NB < last ? NB : last) : (m2 + 1) * NB - 1;
-                        if (i == at) wreg[slot][m2] = load_wf(wsrc + m2 * cb_stride);
+                        if (i == at && wload) wreg[slot][m2] = load_wf(wsrc + m2 * cb_stride);
                     }
-                    if constexpr (SPREAD) {
+                    if constexpr (SPREAD && MORE) {
                         // halo chunk e goes out right after weight row 0, so
                         // the wait for weight row 1 of the same step (PD steps
                         // later) covers it and its store needs no extra wait
@@ -358,8 +357,8 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
             // as soon as its loads are covered by a wait this step needs anyway
             // (they were issued before the weights of step PD); nobody reads
             // that buffer after the previous stage's barrier.
-            if constexpr (!SPREAD) {
-                if (e == C::HALO_STORE_STEP && more) store_halo(buf ^ 1);
+            if constexpr (!SPREAD && MORE) {
+                if (e == C::HALO_STORE_STEP) store_halo(buf ^ 1);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (e + 1 < C::KS) {
@@ -369,7 +368,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         }
         lds_barrier();
         wcur = wnext;
-    }
+    };
+    for (int st = 0; st + 1 < nst; ++st) run_stage(st, std::true_type{});
+    run_stage(nst - 1, std::false_type{});
 
     // ---- split K: each half finishes half of the pixel blocks.  Wave wk
     // exports to LDS the blocks the other half finishes; after the barrier it
