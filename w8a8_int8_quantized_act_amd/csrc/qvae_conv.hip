@@ -52,16 +52,18 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
+// (fields in the order the prologue needs them, so its first scalar loads
+// fetch them together)
 struct ConvArgs {
-    const int8_t *xq;
-    const int8_t *cache;
     const int8_t *wq;       // packed [Cout/32][kt][Cin/32][kh*kw][64 lanes][16 bytes]
     const float *x_scale;
     const float *w_scale;
     const float *bias;
+    const int8_t *xq;
+    const int8_t *cache;
     void *out;
-    int N, T, H, W, Cin, Cout, kt;
-    int tiles_w, tiles_h, co_tiles;
+    int co_tiles, T, H, W, Cin, Cout, kt, N;
+    int tiles_w, tiles_h;
 };
 
 // Halo pixels are stored with a 48-byte pitch (32 data bytes + 16 unused):
@@ -120,18 +122,20 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
 
     const int tid = threadIdx.x;
-    // ---- which tile: output-channel tile fastest, so with an even number of
-    // channel tiles each XCD (workgroups are dealt round-robin over 8 XCDs)
-    // keeps to the same weight slice in its L2.
-    int b = blockIdx.x;
-    const int cot = b % a.co_tiles;
-    b /= a.co_tiles;
-    const int twi = b % a.tiles_w;
-    b /= a.tiles_w;
-    const int thi = b % a.tiles_h;
-    b /= a.tiles_h;
-    const int t = b % a.T;
-    const int n = b / a.T;
+    // all arguments in scalar registers before anything else: one batch of
+    // scalar loads and one wait, instead of a wait at each first use
+    asm volatile("" ::"s"(a.wq), "s"(a.x_scale), "s"(a.w_scale), "s"(a.bias), "s"(a.xq), "s"(a.cache), "s"(a.out),
+                 "s"(a.co_tiles), "s"(a.T), "s"(a.H), "s"(a.W), "s"(a.Cin), "s"(a.Cout), "s"(a.kt), "s"(a.N));
+    // ---- which tile: grid x = channel tile + co_tiles * tile column (the
+    // channel tile fastest, so with an even number of channel tiles each XCD,
+    // dealt workgroups round-robin over 8 XCDs, keeps to the same weight slice
+    // in its L2), y = tile row, z = frame t + T * sample n.
+    const int bx = blockIdx.x;
+    const int twi = bx / a.co_tiles;
+    const int cot = bx - twi * a.co_tiles;
+    const int thi = blockIdx.y;
+    const int n = (int)blockIdx.z / a.T;
+    const int t = (int)blockIdx.z - n * a.T;
     const int h0 = thi * TH, w0 = twi * TW, co0 = cot * C::BCO;
     const int H = a.H, W = a.W, Cin = a.Cin, kt = a.kt;
 
@@ -140,6 +144,69 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     const int S = Cin >> 5;                       // 32-channel slices (a multiple of SL)
     const int nsp = S / C::SL;                    // stages per temporal tap
     const int nst = (kt - i_lo) * nsp;
+
+    // ---- wave roles (wave-uniform: keep them in scalar registers so every
+    // branch on them is a scalar branch and the unrolled K loop stays
+    // straight-line code)
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wk = wave / (WCO * WPX);
+    const int wr = wave - wk * (WCO * WPX);
+    const int wco = wr % WCO, wpx = wr / WCO;
+    const int lrow = lane & 31, lhalf = lane >> 5;
+
+    // weights: fragment (co block cb, tap i, slice s, spatial tap) at
+    // ((((cb * kt + i) * S + s) * KHW + tap) * 64 + lane) * 16.  Within one
+    // stage a wave walks KS consecutive fragments, so the k-step e of stage st
+    // is at wstage(st) + e * 1 KB.
+    // The loads are raw buffer loads from this wave's weight slab: the
+    // offset of a fragment is wave-uniform (a scalar operand) and the lane's
+    // 16 bytes are a constant vector offset, so a load needs no address
+    // arithmetic.
+    const int cb_stride = kt * S * C::KHW * 1024;          // bytes per 32-channel block (< 2^23)
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
+    const int wlane = lane * 16;
+    auto wstage = [&](int st) -> int {
+        const int it = st / nsp;
+        const int p = st - it * nsp;
+        return (((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
+    };
+    auto load_wf = [&](int off) -> v4i {
+        return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off, 0));
+    };
+    v4i wreg[C::PD][MB];
+
+    // ---- prologue loads: the epilogue's factors (a few words, issued first
+    // so their latency hides under the rest), the weight ring, then the first
+    // stage's halo.  The factor products are formed only after the halo's
+    // wait, so no load waits for another.  The factors and biases of this
+    // tile's channels go to LDS with the first halo.
+    constexpr int FPT = (C::BCO + NT - 1) / NT;
+    float *s_fac = reinterpret_cast<float *>(smem + C::LDS_WORK);
+    float f_ws[FPT], f_b[FPT];
+    float sx = 0.0f;
+    if constexpr (!ACC32) {
+        sx = *a.x_scale;
+#pragma unroll
+        for (int k = 0; k < FPT; ++k) {
+            const int c = tid + k * NT;
+            f_ws[k] = 0.0f;
+            f_b[k] = 0.0f;
+            if (c < C::BCO) {
+                f_ws[k] = a.w_scale[co0 + c];
+                if (a.bias) f_b[k] = a.bias[co0 + c];
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    int wcur = wstage(0);
+#pragma unroll
+    for (int e = 0; e < C::PD; ++e)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- halo load descriptors (stage independent parts).  Chunk u covers
     // pixel q = u / (2*SL) and 16 bytes c = u % (2*SL) of its SL slices, so
@@ -194,37 +261,8 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         for (int k = 0; k < C::HALO_PT; ++k) store_chunk(buf, k);
     };
 
-    // ---- wave roles (wave-uniform: keep them in scalar registers so every
-    // branch on them is a scalar branch and the unrolled K loop stays
-    // straight-line code)
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wk = wave / (WCO * WPX);
-    const int wr = wave - wk * (WCO * WPX);
-    const int wco = wr % WCO, wpx = wr / WCO;
-    const int lrow = lane & 31, lhalf = lane >> 5;
-
-    // weights: fragment (co block cb, tap i, slice s, spatial tap) at
-    // ((((cb * kt + i) * S + s) * KHW + tap) * 64 + lane) * 16.  Within one
-    // stage a wave walks KS consecutive fragments, so the k-step e of stage st
-    // is at wstage(st) + e * 1 KB.
-    // The loads are raw buffer loads from this wave's weight slab: the
-    // offset of a fragment is wave-uniform (a scalar operand) and the lane's
-    // 16 bytes are a constant vector offset, so a load needs no address
-    // arithmetic.
-    const int cb_stride = kt * S * C::KHW * 1024;          // bytes per 32-channel block (< 2^23)
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
-    const int wlane = lane * 16;
-    auto wstage = [&](int st) -> int {
-        const int it = st / nsp;
-        const int p = st - it * nsp;
-        return (((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
-    };
-    auto load_wf = [&](int off) -> v4i {
-        return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off, 0));
-    };
-    v4i wreg[C::PD][MB];
+    load_halo(0);
+    __builtin_amdgcn_sched_barrier(0);
 
     // B fragment base offsets (pixel of lane, within the stage buffer)
     int b_q0[NB];
@@ -241,39 +279,15 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
 
-    // rescale factors and biases of this tile's channels (for the epilogue):
-    // loaded first, stored to LDS once the prologue's own waits cover them
-    constexpr int FPT = (C::BCO + NT - 1) / NT;
-    float *s_fac = reinterpret_cast<float *>(smem + C::LDS_WORK);
-    float fac_s[FPT], fac_b[FPT];
-    if constexpr (!ACC32) {
-        const float sx = *a.x_scale;
-#pragma unroll
-        for (int k = 0; k < FPT; ++k) {
-            const int c = tid + k * NT;
-            fac_s[k] = 0.0f;
-            fac_b[k] = 0.0f;
-            if (c < C::BCO) {
-                fac_s[k] = sx * a.w_scale[co0 + c];
-                if (a.bias) fac_b[k] = a.bias[co0 + c];
-            }
-        }
-    }
-
-    int wcur = wstage(0);
-#pragma unroll
-    for (int e = 0; e < C::PD; ++e)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
-    load_halo(0);
     store_halo(0);
+    __builtin_amdgcn_sched_barrier(0);
     if constexpr (!ACC32) {
 #pragma unroll
         for (int k = 0; k < FPT; ++k) {
             const int c = tid + k * NT;
             if (c < C::BCO) {
-                s_fac[c] = fac_s[k];
-                s_fac[C::BCO + c] = fac_b[k];
+                s_fac[c] = sx * f_ws[k];
+                s_fac[C::BCO + c] = f_b[k];
             }
         }
     }
@@ -516,14 +530,15 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     a.tiles_w = (a.W + TW - 1) / TW;
     a.tiles_h = (a.H + TH - 1) / TH;
     a.co_tiles = a.Cout / C::BCO;
-    const int64_t blocks = (int64_t)a.co_tiles * a.tiles_w * a.tiles_h * a.T * a.N;
-    if (blocks <= 0 || blocks > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
+    const int64_t gx = (int64_t)a.co_tiles * a.tiles_w, gz = (int64_t)a.T * a.N;
+    if (gx > 0x7FFFFFFF || a.tiles_h > 65535 || gz > 65535) return QVAE_EUNSUPPORTED;
+    const dim3 grid((unsigned)gx, (unsigned)a.tiles_h, (unsigned)gz);
     if (acc32)
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>),
-                           dim3((unsigned)blocks), dim3(C::NT), 0, st, a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>), grid, dim3(C::NT), 0, st,
+                           a);
     else
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>),
-                           dim3((unsigned)blocks), dim3(C::NT), 0, st, a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>), grid, dim3(C::NT), 0,
+                           st, a);
     return launch_status();
 }
 
