@@ -227,6 +227,27 @@ def main():
     _, quant_avg = timed(quant_pass, args.steps)
     conv_tops = cnt["ops"] / (conv_avg * 1e-3) / 1e12
 
+    # quant passes with a cold last-level cache: before each rep a 1 GiB
+    # scratch buffer is written on the same stream (evicting the 256 MB
+    # Infinity Cache), then one launch is bracketed by two events (the
+    # first fires when the fill has finished); median over the reps
+    def cold(fn, reps=10):
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ts = []
+        for i in range(reps):
+            scratch.fill_(i & 0xFF)
+            e0.record(stream)
+            assert fn() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        del scratch
+        return float(np.median(ts))
+
+    absmax_cold = cold(absmax_pass)
+    quant_cold = cold(quant_pass)
+
     # the same step replayed from a HIP graph (launch overhead removed)
     graph_ms = None
     try:
@@ -296,9 +317,14 @@ def main():
             "absmax_GBs": round(cnt["absmax_bytes"] / (absmax_avg * 1e-3) / 1e9, 1),
             "quantize_ms": round(quant_avg, 5),
             "quantize_GBs": round(cnt["quant_bytes"] / (quant_avg * 1e-3) / 1e9, 1),
+            "absmax_cold_ms": round(absmax_cold, 5),
+            "absmax_cold_GBs": round(cnt["absmax_bytes"] / (absmax_cold * 1e-3) / 1e9, 1),
+            "quantize_cold_ms": round(quant_cold, 5),
+            "quantize_cold_GBs": round(cnt["quant_bytes"] / (quant_cold * 1e-3) / 1e9, 1),
             "hbm_peak_GBs": PEAK_HBM_GBS,
-            "note": "back-to-back launches, warm: a tensor under 256 MB may be partly resident in the "
-                    "last-level cache",
+            "note": "absmax_/quantize_ms: back-to-back launches, warm (a tensor under 256 MB may be partly "
+                    "resident in the last-level cache); *_cold: one launch between two events after a 1 GiB "
+                    "write evicted the last-level cache, median of 10 (dispatch latency included)",
         },
         "first_call_ms": round(first_ms, 3),
     }

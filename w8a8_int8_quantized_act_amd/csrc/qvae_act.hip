@@ -17,9 +17,10 @@
 //                       hundreds of same-address atomics serialize in L2 and
 //                       cost more than the whole pass).
 //   pass 2  k_quantize  every workgroup reduces the <= 512 partials (2 KB from
-//                       L2), derives s, and quantizes: 32 bytes of bf16 in,
-//                       16 int8 codes out per lane.  Workgroup 0 publishes the
-//                       maximum and the scale.
+//                       L2), derives s, and quantizes: 16 bytes of bf16 in,
+//                       8 int8 codes out per lane and load, four loads in
+//                       flight.  Workgroup 0 publishes the maximum and the
+//                       scale.
 //
 // The quotient x / s is the IEEE binary32 one.  The kernel computes t = x * r
 // with r = fl(1 / s) and keeps rne(t) when t is far from a rounding boundary:
@@ -101,43 +102,83 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
 }
 
-// One activation code: clamp(rne(x / s), -127, 127).
-__device__ __forceinline__ int quant_code(float x, float s, float r, bool exact_only)
+// One activation code by the definition: clamp(rne(fl(x / s)), -127, 127).
+__device__ __forceinline__ int quant_code_exact(float x, float s)
 {
-    float t = x * r;
-    float n = __builtin_rintf(t);
-    float dist = fabsf(fabsf(t - n) - 0.5f);       // distance to the nearest half-integer
-    if (exact_only || !(dist > fabsf(t) * 0x1p-20f)) {
-        t = x / s;                                   // correctly rounded division
-        n = __builtin_rintf(t);
-    }
-    n = fminf(fmaxf(n, -127.0f), 127.0f);
-    return (int)n;
+    const float n = __builtin_rintf(x / s);
+    return (int)fminf(fmaxf(n, -127.0f), 127.0f);
 }
 
-__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s, float r, bool ex)
+// Fast path for 8 bf16 values (one 16-byte load) -> 8 codes (two words).
+//   t  = med3(x * r, -127, 127)     clamping first is exact: the code of any
+//                                   |x/s| >= 127 is +-127 either way, and a
+//                                   clamped t sits 0.5 from every boundary
+//   m  = t + 1.5 * 2^23             rounds t to an integer (round to nearest
+//                                   even); the low byte of m's bits is the
+//                                   two's-complement code
+//   d  = |t - (m - 1.5 * 2^23)| - 0.5   minus the distance to the nearest half-integer
+//   f  = |d| - |t| * 2^-20           negative when t is too close to a rounding
+//                                   boundary for fl(x * r) to stand in for fl(x / s)
+// The smallest f of the 8 values is returned in fmin; the caller redoes the
+// whole group exactly when it is not positive.
+__device__ __forceinline__ uint2 quant8_fast(u32x4 v, float r, float &fmin)
 {
-    // lo, hi: two words of two bf16 each -> four int8 codes in one word
-    int q0 = quant_code(bf16_bits_to_float(lo & 0xFFFFu), s, r, ex);
-    int q1 = quant_code(bf16_bits_to_float(lo >> 16), s, r, ex);
-    int q2 = quant_code(bf16_bits_to_float(hi & 0xFFFFu), s, r, ex);
-    int q3 = quant_code(bf16_bits_to_float(hi >> 16), s, r, ex);
-    return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-           ((uint32_t)(q3 & 0xFF) << 24);
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    uint32_t code[8];
+    float f = 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t w = v[k >> 1];
+        const float x = __builtin_bit_cast(float, (k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        const float t = __builtin_amdgcn_fmed3f(x * r, -127.0f, 127.0f);
+        const float m = t + kMagic;
+        const float d = fabsf(t - (m - kMagic)) - 0.5f;
+        f = fminf(f, __builtin_fmaf(fabsf(t), -0x1p-20f, fabsf(d)));
+        code[k] = __builtin_bit_cast(uint32_t, m);
+    }
+    fmin = f;
+    // byte 0 of each word -> packed: sel 0x00/0x04 pick byte 0 of the second/first operand, 0x0C gives zero
+    const uint32_t lo01 = __builtin_amdgcn_perm(code[1], code[0], 0x0C0C0400u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(code[3], code[2], 0x0C0C0400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(code[5], code[4], 0x0C0C0400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(code[7], code[6], 0x0C0C0400u);
+    return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+}
+
+__device__ __forceinline__ uint2 quant8_exact(u32x4 v, float s)
+{
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t w = v[k >> 1];
+        const float x = __builtin_bit_cast(float, (k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        o[k >> 2] |= (uint32_t)(quant_code_exact(x, s) & 0xFF) << (8 * (k & 3));
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+__device__ __forceinline__ uint2 quant8(u32x4 v, float s, float r, bool exact_only)
+{
+    float fmin;
+    uint2 o = quant8_fast(v, r, fmin);
+    if (exact_only || !(fmin > 0.0f)) o = quant8_exact(v, s);
+    return o;
 }
 
 constexpr int kQuantThreads = 256;
+constexpr int kQuantUnroll = 4;   // 16-byte loads in flight per lane
 
-// Each lane: 16 bf16 (two 16-byte loads) -> 16 codes (one 16-byte store).
+// Each lane: 8 bf16 per 16-byte load -> 8 codes per 8-byte store; a wave's
+// load instruction covers 1 KB of contiguous input.
 __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restrict__ x16,
-                                                           int64_t n32,   // groups of 16 elements
+                                                           int64_t n16,   // groups of 8 elements
                                                            const uint16_t *__restrict__ x,
                                                            int64_t numel,
                                                            float clip_ratio,
                                                            uint32_t *__restrict__ absmax,
                                                            int nparts,
                                                            float *__restrict__ x_scale,
-                                                           u32x4 *__restrict__ q16,
+                                                           uint2 *__restrict__ q8,
                                                            int8_t *__restrict__ q)
 {
     // the tensor's maximum from the absmax pass's partial maxima
@@ -156,26 +197,23 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
     }
 
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    for (int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; i < n32; i += stride) {
-        u32x4 v0 = __builtin_nontemporal_load(&x16[2 * i]);
-        u32x4 v1 = __builtin_nontemporal_load(&x16[2 * i + 1]);
-        u32x4 o;
-        if (zero) {
-            o = u32x4{0u, 0u, 0u, 0u};
-        } else {
-            o.x = quant4(v0.x, v0.y, s, r, exact_only);
-            o.y = quant4(v0.z, v0.w, s, r, exact_only);
-            o.z = quant4(v1.x, v1.y, s, r, exact_only);
-            o.w = quant4(v1.z, v1.w, s, r, exact_only);
+    int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    if (zero) {
+        for (; i < n16; i += stride) q8[i] = make_uint2(0u, 0u);
+    } else {
+        for (; i + (kQuantUnroll - 1) * stride < n16; i += kQuantUnroll * stride) {
+            u32x4 v[kQuantUnroll];
+#pragma unroll
+            for (int u = 0; u < kQuantUnroll; ++u) v[u] = __builtin_nontemporal_load(&x16[i + u * stride]);
+#pragma unroll
+            for (int u = 0; u < kQuantUnroll; ++u) q8[i + u * stride] = quant8(v[u], s, r, exact_only);
         }
-        q16[i] = o;
+        for (; i < n16; i += stride) q8[i] = quant8(x16[i], s, r, exact_only);
     }
-    // the last numel % 16 elements, one per lane of workgroup 0
+    // the last numel % 8 elements, one per lane of workgroup 0
     if (blockIdx.x == 0) {
-        int64_t e = n32 * 16 + threadIdx.x;
-        if (e < numel) {
-            q[e] = zero ? 0 : (int8_t)quant_code(bf16_bits_to_float(x[e]), s, r, exact_only);
-        }
+        const int64_t e = n16 * 8 + threadIdx.x;
+        if (e < numel) q[e] = zero ? 0 : (int8_t)quant_code_exact(bf16_bits_to_float(x[e]), s);
     }
 }
 
@@ -202,13 +240,15 @@ extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ra
     if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
     if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
-    const int64_t n32 = numel / 16;
-    int64_t want = (n32 + kQuantThreads - 1) / kQuantThreads;
-    int64_t cap = (int64_t)device_cus() * 16;
-    int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+    const int64_t n16 = numel / 8;
+    // enough workgroups for every lane to have kQuantUnroll loads in flight,
+    // at most 8 per CU (one grid-stride sweep of the tensor per unrolled pass)
+    int64_t want = (n16 + (int64_t)kQuantThreads * kQuantUnroll - 1) / ((int64_t)kQuantThreads * kQuantUnroll);
+    const int64_t cap = (int64_t)device_cus() * 8;
+    const int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, as_stream(stream),
-                       reinterpret_cast<const u32x4 *>(x), n32, x, numel, clip_ratio, absmax, absmax_blocks(numel),
-                       x_scale, reinterpret_cast<u32x4 *>(xq), xq);
+                       reinterpret_cast<const u32x4 *>(x), n16, x, numel, clip_ratio, absmax, absmax_blocks(numel),
+                       x_scale, reinterpret_cast<uint2 *>(xq), xq);
     return launch_status();
 }
 
