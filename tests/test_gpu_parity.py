@@ -269,6 +269,42 @@ def _compare_full(ops, ci, r, n_random=1500, seed=0, cache_zero=False):
     return pos
 
 
+@pytest.mark.parametrize("shape,cache_kind", [
+    ((2, 384, 3, 60, 120), None),      # 384 ragged 8x16 tiles: workgroups run several, frames with 1..3 taps
+    ((2, 384, 3, 60, 120), "random"),  # the same with a nonzero prev-frame cache (all taps valid)
+    ((1, 192, 2, 250, 136), None),     # 288 ragged 16x16 tiles of 192 channels
+])
+def test_conv_several_tiles_per_workgroup(ops, shape, cache_kind):
+    """Shapes with more pixel tiles than CUs, so a workgroup runs tiles in a
+    row and prefetches the next tile's first halo and weights; checked against
+    the oracle on sampled positions (tile seams, ragged edges, every frame)."""
+    N, C, T, H, W = shape
+    ci = wl.draw_custom(70 + C + (1 if cache_kind else 0), N, C, C, T, H, W)
+    spec = ci.spec
+    wq, ws = oracle.quantize_weights(ci.w)
+    a, s, xq = oracle.act_absmax_quant(ci.x)
+    cache = None
+    if cache_kind == "random":
+        g = np.random.default_rng(5)
+        cache = g.integers(-127, 128, (N, 2, H, W, C)).astype(np.int8)
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    _, xs_d, xq_d = ops.act_absmax_quant(to_dev_bits(ci.x))
+    b_d = torch.from_numpy(ci.b).to(DEV)
+    cache_d = None if cache is None else torch.from_numpy(cache).to(DEV)
+    y = ops.causalconv3d_w8a8(xq_d, xs_d, wq_d, ws_d, b_d, cache_d)
+    acc = ops.causalconv3d_w8a8_acc32(xq_d, wq_d, cache_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(xq_d.cpu().numpy(), xq)
+    pos = sample_positions(N, T, H, W, 300, 7)
+    ref_acc = oracle.conv_acc(xq, wq, cache, positions=pos)
+    ref_y = oracle.epilogue(ref_acc, s, ws, ci.b)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    got_acc = acc.reshape(-1, C)[pos_d].cpu().numpy()
+    got_y = bf16_bits(y.reshape(-1, C)[pos_d])
+    assert np.array_equal(got_acc, ref_acc), f"{np.count_nonzero(got_acc != ref_acc)} accumulators differ"
+    assert ulp_dist(got_y, ref_y).max() == 0
+
+
 def test_workload_single_96_t4_32_full(ops):
     ci = wl.draw_workload("single_96_t4_32")[0]
     r = _run_full_conv(ops, ci)

@@ -43,6 +43,7 @@
 // quad, so the epilogue writes 4 bf16 (8 bytes) per store along the
 // channels-last output.
 #include <type_traits>
+#include <utility>
 
 #include "qvae_internal.h"
 
@@ -51,6 +52,20 @@ namespace qvae {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): the index
+// is a compile-time constant in every call, so arrays it selects from stay in
+// registers whatever the surrounding loops look like to the optimizer
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // (fields in the order the prologue needs them, so its first scalar loads
 // fetch them together)
@@ -103,14 +118,21 @@ struct ConvCfg {
     static constexpr int XB = ACC_BYTES / 2;
     static constexpr int RED_BYTES = (WK > 1) ? WCO * WPX * 2 * XB : 0;
     static_assert(WK == 1 || NB % 2 == 0, "split K shares the pixel blocks between the two halves");
-    // epilogue staging: 32 pixel rows of one wave's channels (INT32 worst case)
-    static constexpr int EPI_WAVE_BYTES = 32 * (MB * 32 * 4 + 16);
-    static constexpr int EPI_BYTES = WCO * WPX * EPI_WAVE_BYTES;
-    static constexpr int LDS_MAIN = (2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES;
-    static constexpr int LDS_WORK = (LDS_MAIN > EPI_BYTES) ? LDS_MAIN : EPI_BYTES;
     // per-channel rescale factors fl(s_x * s_w[co]) and biases of the tile
     static constexpr int FAC_BYTES = 2 * BCO * 4;
-    static constexpr int LDS_BYTES = LDS_WORK + FAC_BYTES;
+    // LDS layout, elem = output bytes per value:
+    //   WK = 1: [halo buffer 0][halo buffer 1][epilogue staging, a slice per wave][factors]
+    //           separate regions: a workgroup that runs several tiles holds the
+    //           next tile's first halo in a buffer while it finishes this one
+    //   WK = 2: [halo buffers and split-K export slices, overlapped][factors]
+    //           (one tile per workgroup; the exports start after the last stage)
+    static constexpr int epi_wave_bytes(int elem) { return 32 * (MB * 32 * elem + 16); }
+    static constexpr int work_bytes(int elem)
+    {
+        return WK > 1 ? ((2 * BUF_BYTES > RED_BYTES) ? 2 * BUF_BYTES : RED_BYTES)
+                      : 2 * BUF_BYTES + WCO * WPX * epi_wave_bytes(elem);
+    }
+    static constexpr int lds_bytes(int elem) { return work_bytes(elem) + FAC_BYTES; }
 };
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
@@ -119,31 +141,58 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     constexpr int NT = C::NT;
     constexpr int PH = (KH - 1) / 2, PW = (KW - 1) / 2;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+    constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
+    constexpr int WORK = C::work_bytes(ELEM);
+    // Several tiles per workgroup for the large wave tiles (one workgroup per
+    // CU: nothing else hides a tile's prologue).  Split K runs one tile; the
+    // small tiles run two workgroups per CU, which overlap each other's
+    // prologues and epilogues, and carrying the weight ring across tiles would
+    // cost them that second workgroup.
+    constexpr bool PERSIST = WK == 1 && MB * NB >= 12;
+    __shared__ __attribute__((aligned(16))) char smem[C::lds_bytes(ELEM)];
 
     const int tid = threadIdx.x;
     // all arguments in scalar registers before anything else: one batch of
     // scalar loads and one wait, instead of a wait at each first use
     asm volatile("" ::"s"(a.wq), "s"(a.x_scale), "s"(a.w_scale), "s"(a.bias), "s"(a.xq), "s"(a.cache), "s"(a.out),
-                 "s"(a.co_tiles), "s"(a.T), "s"(a.H), "s"(a.W), "s"(a.Cin), "s"(a.Cout), "s"(a.kt), "s"(a.N));
-    // ---- which tile: grid x = channel tile + co_tiles * tile column (the
-    // channel tile fastest, so with an even number of channel tiles each XCD,
-    // dealt workgroups round-robin over 8 XCDs, keeps to the same weight slice
-    // in its L2), y = tile row, z = frame t + T * sample n.
-    const int bx = blockIdx.x;
-    const int twi = bx / a.co_tiles;
-    const int cot = bx - twi * a.co_tiles;
-    const int thi = blockIdx.y;
-    const int n = (int)blockIdx.z / a.T;
-    const int t = (int)blockIdx.z - n * a.T;
-    const int h0 = thi * TH, w0 = twi * TW, co0 = cot * C::BCO;
+                 "s"(a.co_tiles), "s"(a.T), "s"(a.H), "s"(a.W), "s"(a.Cin), "s"(a.Cout), "s"(a.kt), "s"(a.N),
+                 "s"(a.tiles_w), "s"(a.tiles_h));
+    // ---- tiles.  Pixel tiles are numbered pt = column + tiles_w * (row +
+    // tiles_h * (t + T * n)).  Workgroup b runs channel tile b % co_tiles and
+    // pixel tiles b / co_tiles + k * (gridDim.x / co_tiles), k = 0, 1, ...
+    // (the grid is a multiple of co_tiles; with split K, or when one round of
+    // workgroups covers the frame, each runs one tile).  The channel tile is
+    // fastest in the workgroup index, so with an even number of channel tiles
+    // each XCD (workgroups are dealt round-robin over 8 XCDs) keeps to the
+    // same weight slice in its L2.
+    const int cot = blockIdx.x % a.co_tiles;
+    const int pstride = gridDim.x / a.co_tiles;
+    const int nptiles = a.tiles_w * a.tiles_h * a.T * a.N;
+    const int co0 = cot * C::BCO;
     const int H = a.H, W = a.W, Cin = a.Cin, kt = a.kt;
-
-    // valid temporal taps: frame t-(kt-1)+i exists, or comes from the cache
-    const int i_lo = a.cache ? 0 : max(0, kt - 1 - t);
     const int S = Cin >> 5;                       // 32-channel slices (a multiple of SL)
     const int nsp = S / C::SL;                    // stages per temporal tap
-    const int nst = (kt - i_lo) * nsp;
+    struct Tile {
+        int h0, w0, t, n;
+        int i_lo;   // first temporal tap: frame t-(kt-1)+i exists, or comes from the cache
+        int nst;    // K stages
+    };
+    auto decode = [&](int ptile) {
+        Tile tl;
+        const int tw = ptile % a.tiles_w;
+        int r = ptile / a.tiles_w;
+        const int th = r % a.tiles_h;
+        r /= a.tiles_h;
+        tl.t = r % a.T;
+        tl.n = r / a.T;
+        tl.h0 = th * TH;
+        tl.w0 = tw * TW;
+        tl.i_lo = a.cache ? 0 : max(0, kt - 1 - tl.t);
+        tl.nst = (kt - tl.i_lo) * nsp;
+        return tl;
+    };
+    int pt = blockIdx.x / a.co_tiles;
+    Tile cur = decode(pt);
 
     // ---- wave roles (wave-uniform: keep them in scalar registers so every
     // branch on them is a scalar branch and the unrolled K loop stays
@@ -158,7 +207,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     // weights: fragment (co block cb, tap i, slice s, spatial tap) at
     // ((((cb * kt + i) * S + s) * KHW + tap) * 64 + lane) * 16.  Within one
     // stage a wave walks KS consecutive fragments, so the k-step e of stage st
-    // is at wstage(st) + e * 1 KB.
+    // is at wstage(tile, st) + e * 1 KB.
     // The loads are raw buffer loads from this wave's weight slab: the
     // offset of a fragment is wave-uniform (a scalar operand) and the lane's
     // 16 bytes are a constant vector offset, so a load needs no address
@@ -167,10 +216,10 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
     const int wlane = lane * 16;
-    auto wstage = [&](int st) -> int {
+    auto wstage = [&](const Tile &tl, int st) -> int {
         const int it = st / nsp;
         const int p = st - it * nsp;
-        return (((i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
+        return (((tl.i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
     };
     auto load_wf = [&](int off) -> v4i {
         return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off, 0));
@@ -183,7 +232,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     // wait, so no load waits for another.  The factors and biases of this
     // tile's channels go to LDS with the first halo.
     constexpr int FPT = (C::BCO + NT - 1) / NT;
-    float *s_fac = reinterpret_cast<float *>(smem + C::LDS_WORK);
+    float *s_fac = reinterpret_cast<float *>(smem + WORK);
     float f_ws[FPT], f_b[FPT];
     float sx = 0.0f;
     if constexpr (!ACC32) {
@@ -201,7 +250,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    int wcur = wstage(0);
+    int wcur = wstage(cur, 0);
 #pragma unroll
     for (int e = 0; e < C::PD; ++e)
 #pragma unroll
@@ -217,31 +266,39 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     constexpr uint32_t kOutside = 0x80000000u;   // >= any frame size (frames are < 2^31 bytes)
     uint32_t h_off[C::HALO_PT];   // byte offset from the stage's slice base, kOutside = zero pixel
     int h_lds[C::HALO_PT];        // LDS byte offset inside a stage buffer (idle lanes: slice padding)
+    auto set_hoff = [&](const Tile &tl) {
+#pragma unroll
+        for (int k = 0; k < C::HALO_PT; ++k) {
+            const int u = tid + k * NT;
+            h_off[k] = kOutside;
+            if (u < C::HALO_CHUNKS) {
+                const int q = u / (2 * C::SL), c = u - q * (2 * C::SL);
+                const int hh = q / C::HWD, ww = q - hh * C::HWD;
+                const int gh = tl.h0 - PH + hh, gw = tl.w0 - PW + ww;
+                if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (uint32_t)((gh * W + gw) * Cin + c * 16);
+            }
+        }
+    };
 #pragma unroll
     for (int k = 0; k < C::HALO_PT; ++k) {
         const int u = tid + k * NT;
-        h_off[k] = kOutside;
         h_lds[k] = C::HALO_PAD;
         if (u < C::HALO_CHUNKS) {
             const int q = u / (2 * C::SL), c = u - q * (2 * C::SL);
-            const int sl = c >> 1, half = c & 1;
-            const int hh = q / C::HWD, ww = q - hh * C::HWD;
-            const int gh = h0 - PH + hh, gw = w0 - PW + ww;
-            h_lds[k] = sl * C::SLICE_BYTES + q * kHaloPitch + half * 16;
-            if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (uint32_t)((gh * W + gw) * Cin + c * 16);
+            h_lds[k] = (c >> 1) * C::SLICE_BYTES + q * kHaloPitch + (c & 1) * 16;
         }
     }
     const size_t frame_bytes = (size_t)H * W * Cin;
-    auto frame_ptr = [&](int i) -> const int8_t * {
-        const int tau = t - (kt - 1) + i;
-        if (tau >= 0) return a.xq + ((size_t)n * a.T + tau) * frame_bytes;
-        return a.cache + ((size_t)n * (kt - 1) + (kt - 1 + tau)) * frame_bytes;
+    auto frame_ptr = [&](const Tile &tl, int i) -> const int8_t * {
+        const int tau = tl.t - (kt - 1) + i;
+        if (tau >= 0) return a.xq + ((size_t)tl.n * a.T + tau) * frame_bytes;
+        return a.cache + ((size_t)tl.n * (kt - 1) + (kt - 1 + tau)) * frame_bytes;
     };
     v4i hreg[C::HALO_PT];
-    auto halo_rsrc = [&](int st) {
+    auto halo_rsrc = [&](const Tile &tl, int st) {
         const int it = st / nsp;
         const int p = st - it * nsp;
-        const int8_t *fps = frame_ptr(i_lo + it) + p * C::SL * 32;
+        const int8_t *fps = frame_ptr(tl, tl.i_lo + it) + p * C::SL * 32;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(fps), 0,
                                                  (int)(frame_bytes - (size_t)p * C::SL * 32), 0x00020000);
     };
@@ -251,8 +308,8 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     auto store_chunk = [&](int buf, int k) {
         *reinterpret_cast<v4i *>(smem + buf * C::BUF_BYTES + h_lds[k]) = hreg[k];
     };
-    auto load_halo = [&](int st) {
-        const __amdgpu_buffer_rsrc_t rs = halo_rsrc(st);
+    auto load_halo = [&](const Tile &tl, int st) {
+        const __amdgpu_buffer_rsrc_t rs = halo_rsrc(tl, st);
 #pragma unroll
         for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rs, k);
     };
@@ -261,7 +318,8 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         for (int k = 0; k < C::HALO_PT; ++k) store_chunk(buf, k);
     };
 
-    load_halo(0);
+    set_hoff(cur);
+    load_halo(cur, 0);
     __builtin_amdgcn_sched_barrier(0);
 
     // B fragment base offsets (pixel of lane, within the stage buffer)
@@ -307,20 +365,18 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
     };
 
-    // One stage.  MORE = a next stage exists: then its weights enter the ring
-    // in the last PD k-steps and its halo goes to the other buffer.  The last
-    // stage is a separate instantiation without those loads, so the epilogue
-    // never waits for prefetches nobody uses.
+    // One stage on the halo in buffer buf.  MORE = a next stage exists (in this
+    // tile or the workgroup's next one): its weights (ring offset wnext) enter
+    // the ring in the last PD k-steps and its halo (buffer resource rsn, lane
+    // offsets h_off) goes to the other buffer.  The very last stage is a
+    // separate instantiation without those loads, so the epilogue never waits
+    // for prefetches nobody uses.  When the stage has enough k-steps, halo
+    // chunk k of the next stage is loaded in step k and stored to the other
+    // buffer in step k + PD, one instruction per step between two MFMAs;
+    // otherwise all chunks are loaded at the start and stored in one step.
     constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
-    auto run_stage = [&](int st, auto more_c) {
+    auto run_stage = [&](int buf, int wnext, __amdgpu_buffer_rsrc_t rsn, auto more_c) {
         constexpr bool MORE = decltype(more_c)::value;
-        const int buf = st & 1;
-        const int wnext = MORE ? wstage(st + 1) : wcur;
-        // When the stage has enough k-steps, halo chunk k of the next stage is
-        // loaded in step k and stored to the other buffer in step k + PD, one
-        // instruction per step between two MFMAs; otherwise all chunks are
-        // loaded here and stored in one step.
-        const __amdgpu_buffer_rsrc_t rsn = halo_rsrc(MORE ? st + 1 : st);
         if constexpr (!SPREAD && MORE) {
 #pragma unroll
             for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
@@ -383,143 +439,188 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         lds_barrier();
         wcur = wnext;
     };
-    for (int st = 0; st + 1 < nst; ++st) run_stage(st, std::true_type{});
-    run_stage(nst - 1, std::false_type{});
+    // ---- the workgroup's tiles: stages run back to back across tile
+    // boundaries (the last stage of a tile prefetches the next tile's first
+    // halo and weights), the epilogue of a tile runs while that halo waits in
+    // its buffer.
+    auto epilogue = [&](const Tile &tl) __attribute__((always_inline)) {
+        // ---- split K: each half finishes half of the pixel blocks.  Wave wk
+        // exports to LDS the blocks the other half finishes; after the barrier it
+        // reads the other half's export of its own blocks into registers and adds
+        // it while rescaling (INT32 sums, exact in any order).
+        constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
+        v4i part[(WK > 1) ? MB * HB * 4 : 1];
+        if constexpr (WK > 1) {
+            int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
+            const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
+            auto xport = [&](auto wkc) {
+                constexpr int other = 1 - decltype(wkc)::value;
+                static_for<MB>([&](auto mbc) {
+                    static_for<HB>([&](auto jc) {
+                        constexpr int mb = decltype(mbc)::value, j = decltype(jc)::value;
+                        const v16i v = acc[mb][other * HB + j];
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
+                                make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                    });
+                });
+            };
+            if (wk == 0)
+                xport(std::integral_constant<int, 0>{});
+            else
+                xport(std::integral_constant<int, 1>{});
+            lds_barrier();
+#pragma unroll
+            for (int q = 0; q < MB * HB * 4; ++q) {
+                const int4 u = exp_other[q * 64 + lane];
+                part[q] = v4i{u.x, u.y, u.z, u.w};
+            }
+        }
 
-    // ---- split K: each half finishes half of the pixel blocks.  Wave wk
-    // exports to LDS the blocks the other half finishes; after the barrier it
-    // reads the other half's export of its own blocks into registers and adds
-    // it while rescaling (INT32 sums, exact in any order).
-    constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
-    v4i part[(WK > 1) ? MB * HB * 4 : 1];
-    if constexpr (WK > 1) {
-        int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
-        const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
-        auto xport = [&](auto wkc) {
-            constexpr int other = 1 - decltype(wkc)::value;
+        // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
+        // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
+        // block.  Each 32-pixel block is rescaled (one FP32 fma with the
+        // per-channel factor and bias, then bf16 round-to-nearest-even with the
+        // packed convert), written to the wave's LDS staging rows
+        // [pixel][channel], then read back row-wise so every lane stores 16
+        // contiguous bytes and consecutive lanes continue along the channels-last
+        // output row.  The stores are raw buffer stores relative to the tile's
+        // first output: a pixel outside the image gets an offset past the
+        // buffer's size and the hardware drops it, so no lane branches.
+        constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
+        constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
+        constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
+        static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
+        static_assert(32 * EPITCH <= C::epi_wave_bytes(ELEM), "staging rows fit the wave's LDS slice");
+        static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
+        // staging: with split K the partner's export slice (this wave has read it
+        // into registers and nobody else touches it); otherwise a slice per wave
+        char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : 2 * C::BUF_BYTES + wr * C::epi_wave_bytes(ELEM));
+
+        const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
+        const size_t tile_first = ((((size_t)tl.n * a.T + tl.t) * H + tl.h0) * W + tl.w0) * (size_t)a.Cout + cw0;
+        const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
+        const size_t left = (out_total - tile_first) * ELEM;
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
+        const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+        // this lane's per-channel factors and biases: read from LDS once when the
+        // wave tile is large (one wave per SIMD anyway, registers to spare after
+        // the K loop), else at each use so small tiles keep two waves per SIMD
+        constexpr bool HOIST = !ACC32 && MB * NB >= 12;
+        f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
+        if constexpr (HOIST) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                for (int j = 0; j < HB; ++j)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const v16i &v = acc[mb][other * HB + j];
-                        exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
-                            make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
-                    }
-        };
-        if (wk == 0)
-            xport(std::integral_constant<int, 0>{});
-        else
-            xport(std::integral_constant<int, 1>{});
-        lds_barrier();
-#pragma unroll
-        for (int q = 0; q < MB * HB * 4; ++q) {
-            const int4 u = exp_other[q * 64 + lane];
-            part[q] = v4i{u.x, u.y, u.z, u.w};
-        }
-    }
-
-    // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
-    // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
-    // block.  Each 32-pixel block is rescaled (one FP32 fma with the
-    // per-channel factor and bias, then bf16 round-to-nearest-even with the
-    // packed convert), written to the wave's LDS staging rows
-    // [pixel][channel], then read back row-wise so every lane stores 16
-    // contiguous bytes and consecutive lanes continue along the channels-last
-    // output row.  The stores are raw buffer stores relative to the tile's
-    // first output: a pixel outside the image gets an offset past the
-    // buffer's size and the hardware drops it, so no lane branches.
-    constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
-    constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
-    constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
-    constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
-    static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
-    static_assert(32 * EPITCH <= C::EPI_WAVE_BYTES, "staging rows fit the wave's LDS slice");
-    static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
-    // staging: with split K the partner's export slice (this wave has read it
-    // into registers and nobody else touches it); otherwise a slice per wave
-    char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : wr * C::EPI_WAVE_BYTES);
-
-    const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
-    const size_t tile_first = ((((size_t)n * a.T + t) * H + h0) * W + w0) * (size_t)a.Cout + cw0;
-    const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
-    const size_t left = (out_total - tile_first) * ELEM;
-    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-        static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
-    const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
-    typedef float f4 __attribute__((ext_vector_type(4)));
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-    // this lane's per-channel factors and biases: read from LDS once when the
-    // wave tile is large (one wave per SIMD anyway, registers to spare after
-    // the K loop), else at each use so small tiles keep two waves per SIMD
-    constexpr bool HOIST = !ACC32 && MB * NB >= 12;
-    f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
-    if constexpr (HOIST) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
-                fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
-                fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
-            }
-    }
-    // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
-    auto finish_block = [&](auto wkc, int j) {
-        constexpr int WKC = decltype(wkc)::value;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const v16i &x = acc[mb][WKC * HB + j];
-                v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-                if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
-                char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
-                if constexpr (ACC32) {
-                    *reinterpret_cast<v4i *>(dst) = v;
-                } else {
-                    f4 y;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        if constexpr (HOIST) {
-                            y[e] = __builtin_fmaf((float)v[e], fm[mb][g][e], fb[mb][g][e]);
-                        } else {
-                            const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
-                            y[e] = __builtin_fmaf((float)v[e], s_fac[col], s_fac[C::BCO + col]);
-                        }
-                    }
-                    const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
-                    const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
-                    *reinterpret_cast<uint2 *>(dst) =
-                        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                for (int g = 0; g < 4; ++g) {
+                    const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
+                    fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
+                    fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
                 }
-            }
-#pragma unroll
-        for (int k = 0; k < CHUNKS / 64; ++k) {
-            const int c = k * 64 + lane;
-            const int px = c / (ROWB / 16);
-            const int off = (c - px * (ROWB / 16)) * 16;
-            const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
-            const int p = (wpx * NB + WKC * HB + j) * 32 + px;
-            const int pr = p / TW, pc = p - pr * TW;
-            const bool inside = h0 + pr < H && w0 + pc < W;
-            const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, 0);
         }
-    };
-    auto finish_all = [&](auto wkc) {
+        // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
+        auto finish_block = [&](auto wkc, auto jc) {
+            constexpr int WKC = decltype(wkc)::value;
+            constexpr int j = decltype(jc)::value;
 #pragma unroll
-        for (int j = 0; j < HB; ++j) finish_block(wkc, j);
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const v16i &x = acc[mb][WKC * HB + j];
+                    v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                    if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                    char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
+                    if constexpr (ACC32) {
+                        *reinterpret_cast<v4i *>(dst) = v;
+                    } else {
+                        f4 y;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if constexpr (HOIST) {
+                                y[e] = __builtin_fmaf((float)v[e], fm[mb][g][e], fb[mb][g][e]);
+                            } else {
+                                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
+                                y[e] = __builtin_fmaf((float)v[e], s_fac[col], s_fac[C::BCO + col]);
+                            }
+                        }
+                        const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
+                        const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
+                        *reinterpret_cast<uint2 *>(dst) =
+                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                    }
+                }
+#pragma unroll
+            for (int k = 0; k < CHUNKS / 64; ++k) {
+                const int c = k * 64 + lane;
+                const int px = c / (ROWB / 16);
+                const int off = (c - px * (ROWB / 16)) * 16;
+                const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
+                const int p = (wpx * NB + WKC * HB + j) * 32 + px;
+                const int pr = p / TW, pc = p - pr * TW;
+                const bool inside = tl.h0 + pr < H && tl.w0 + pc < W;
+                const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, 0);
+            }
+        };
+        auto finish_all = [&](auto wkc) { static_for<HB>([&](auto jc) { finish_block(wkc, jc); }); };
+        if (WK > 1 && wk == 1)
+            finish_all(std::integral_constant<int, 1>{});
+        else
+            finish_all(std::integral_constant<int, 0>{});
     };
-    if (WK > 1 && wk == 1)
-        finish_all(std::integral_constant<int, 1>{});
-    else
-        finish_all(std::integral_constant<int, 0>{});
+    int gs = 0;   // stages run by this workgroup (buffer parity)
+    for (;;) {
+        for (int st = 0; st + 1 < cur.nst; ++st, ++gs)
+            run_stage(gs & 1, wstage(cur, st + 1), halo_rsrc(cur, st + 1), std::true_type{});
+        // the tile's last stage: prefetch the workgroup's next tile, if any
+        if constexpr (PERSIST) {
+            const int ptn = pt + pstride;
+            if (ptn < nptiles) {
+                const Tile nxt = decode(ptn);
+                set_hoff(nxt);   // this stage's halo loads are the next tile's
+                run_stage(gs & 1, wstage(nxt, 0), halo_rsrc(nxt, 0), std::true_type{});
+                ++gs;
+                epilogue(cur);
+                cur = nxt;
+                pt = ptn;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
+                continue;
+            }
+        }
+        run_stage(gs & 1, wcur, halo_rsrc(cur, cur.nst - 1), std::false_type{});
+        epilogue(cur);
+        break;
+    }
 }
 
+
 // ---- host side ------------------------------------------------------------
+
+// Workgroups of one instantiation that fit on a CU at once (registers, LDS,
+// waves), asked of the runtime once per instantiation.
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
+static int resident_per_cu(bool acc32)
+{
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
+    static int occ[2] = {0, 0};
+    int &o = occ[acc32 ? 1 : 0];
+    if (o == 0) {
+        int n = 0;
+        const void *f = acc32 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>)
+                              : reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>);
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, C::NT, 0) != hipSuccess || n < 1) n = 1;
+        o = n;
+    }
+    return o;
+}
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
 static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
@@ -530,15 +631,22 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     a.tiles_w = (a.W + TW - 1) / TW;
     a.tiles_h = (a.H + TH - 1) / TH;
     a.co_tiles = a.Cout / C::BCO;
-    const int64_t gx = (int64_t)a.co_tiles * a.tiles_w, gz = (int64_t)a.T * a.N;
-    if (gx > 0x7FFFFFFF || a.tiles_h > 65535 || gz > 65535) return QVAE_EUNSUPPORTED;
-    const dim3 grid((unsigned)gx, (unsigned)a.tiles_h, (unsigned)gz);
+    const int64_t nptiles = (int64_t)a.tiles_w * a.tiles_h * a.T * a.N;
+    if (nptiles * a.co_tiles > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
+    int64_t grid = nptiles * a.co_tiles;
+    if (WK == 1 && MB * NB >= 12) {
+        // more tiles than resident workgroups: each workgroup runs several
+        // tiles in a row (the grid stays a multiple of the channel tiles)
+        const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32) /
+                            a.co_tiles;
+        if (per >= 1 && nptiles > per) grid = per * a.co_tiles;
+    }
     if (acc32)
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>), grid, dim3(C::NT), 0, st,
-                           a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>), dim3((unsigned)grid),
+                           dim3(C::NT), 0, st, a);
     else
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>), grid, dim3(C::NT), 0,
-                           st, a);
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>), dim3((unsigned)grid),
+                           dim3(C::NT), 0, st, a);
     return launch_status();
 }
 
