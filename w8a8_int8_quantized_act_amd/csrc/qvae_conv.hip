@@ -136,19 +136,19 @@ struct ConvCfg {
 };
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
-__global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
+__global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 1) void k_conv_igemm(ConvArgs a)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     constexpr int NT = C::NT;
     constexpr int PH = (KH - 1) / 2, PW = (KW - 1) / 2;
     constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
     constexpr int WORK = C::work_bytes(ELEM);
-    // Several tiles per workgroup for the large wave tiles (one workgroup per
-    // CU: nothing else hides a tile's prologue).  Split K runs one tile; the
-    // small tiles run two workgroups per CU, which overlap each other's
-    // prologues and epilogues, and carrying the weight ring across tiles would
-    // cost them that second workgroup.
-    constexpr bool PERSIST = WK == 1 && MB * NB >= 12;
+    // Tiles per workgroup (see the launch): split K runs one (0).  Otherwise a
+    // workgroup runs several, and the last stage of a tile prefetches the next
+    // tile's first halo and, for the large wave tiles, its weight ring too (2).
+    // The small tiles (1) reload the ring after the epilogue instead: holding
+    // it across the epilogue would cost them their second workgroup per CU.
+    constexpr int PERSIST = WK > 1 ? 0 : (MB * NB >= 12 ? 2 : 1);
     __shared__ __attribute__((aligned(16))) char smem[C::lds_bytes(ELEM)];
 
     const int tid = threadIdx.x;
@@ -365,19 +365,19 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
         for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
     };
 
-    // One stage on the halo in buffer buf.  MORE = a next stage exists (in this
-    // tile or the workgroup's next one): its weights (ring offset wnext) enter
-    // the ring in the last PD k-steps and its halo (buffer resource rsn, lane
-    // offsets h_off) goes to the other buffer.  The very last stage is a
-    // separate instantiation without those loads, so the epilogue never waits
+    // One stage on the halo in buffer buf.  MORE > 0: a next stage exists (in
+    // this tile or the workgroup's next one) and its halo (buffer resource rsn,
+    // lane offsets h_off) goes to the other buffer; MORE = 2: its weights (ring
+    // offset wnext) also enter the ring in the last PD k-steps.  The very last
+    // stage is an instantiation without either, so the epilogue never waits
     // for prefetches nobody uses.  When the stage has enough k-steps, halo
     // chunk k of the next stage is loaded in step k and stored to the other
     // buffer in step k + PD, one instruction per step between two MFMAs;
     // otherwise all chunks are loaded at the start and stored in one step.
     constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
     auto run_stage = [&](int buf, int wnext, __amdgpu_buffer_rsrc_t rsn, auto more_c) {
-        constexpr bool MORE = decltype(more_c)::value;
-        if constexpr (!SPREAD && MORE) {
+        constexpr int MORE = decltype(more_c)::value;
+        if constexpr (!SPREAD && MORE > 0) {
 #pragma unroll
             for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
         }
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
 #pragma unroll
         for (int e = 0; e < C::KS; ++e) {
             const int slot = e % C::PD;
-            const bool wload = e + C::PD < C::KS || MORE;
+            const bool wload = e + C::PD < C::KS || MORE == 2;
             const int wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024 : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                         const int at = (m2 == 0) ? (NB < last ? NB : last) : (m2 + 1) * NB - 1;
                         if (i == at && wload) wreg[slot][m2] = load_wf(wsrc + m2 * cb_stride);
                     }
-                    if constexpr (SPREAD && MORE) {
+                    if constexpr (SPREAD && MORE > 0) {
                         // halo chunk e goes out right after weight row 0, so
                         // the wait for weight row 1 of the same step (PD steps
                         // later) covers it and its store needs no extra wait
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
             // as soon as its loads are covered by a wait this step needs anyway
             // (they were issued before the weights of step PD); nobody reads
             // that buffer after the previous stage's barrier.
-            if constexpr (!SPREAD && MORE) {
+            if constexpr (!SPREAD && MORE > 0) {
                 if (e == C::HALO_STORE_STEP) store_halo(buf ^ 1);
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -576,14 +576,14 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
     int gs = 0;   // stages run by this workgroup (buffer parity)
     for (;;) {
         for (int st = 0; st + 1 < cur.nst; ++st, ++gs)
-            run_stage(gs & 1, wstage(cur, st + 1), halo_rsrc(cur, st + 1), std::true_type{});
+            run_stage(gs & 1, wstage(cur, st + 1), halo_rsrc(cur, st + 1), std::integral_constant<int, 2>{});
         // the tile's last stage: prefetch the workgroup's next tile, if any
-        if constexpr (PERSIST) {
+        if constexpr (PERSIST > 0) {
             const int ptn = pt + pstride;
             if (ptn < nptiles) {
                 const Tile nxt = decode(ptn);
                 set_hoff(nxt);   // this stage's halo loads are the next tile's
-                run_stage(gs & 1, wstage(nxt, 0), halo_rsrc(nxt, 0), std::true_type{});
+                run_stage(gs & 1, wstage(nxt, 0), halo_rsrc(nxt, 0), std::integral_constant<int, PERSIST>{});
                 ++gs;
                 epilogue(cur);
                 cur = nxt;
@@ -592,10 +592,17 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64) void k_conv_igemm(ConvArgs a)
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
+                if constexpr (PERSIST == 1) {
+                    wcur = wstage(cur, 0);
+#pragma unroll
+                    for (int e = 0; e < C::PD; ++e)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
+                }
                 continue;
             }
         }
-        run_stage(gs & 1, wcur, halo_rsrc(cur, cur.nst - 1), std::false_type{});
+        run_stage(gs & 1, wcur, halo_rsrc(cur, cur.nst - 1), std::integral_constant<int, 0>{});
         epilogue(cur);
         break;
     }
@@ -634,7 +641,7 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     const int64_t nptiles = (int64_t)a.tiles_w * a.tiles_h * a.T * a.N;
     if (nptiles * a.co_tiles > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
     int64_t grid = nptiles * a.co_tiles;
-    if (WK == 1 && MB * NB >= 12) {
+    if (WK == 1) {
         // more tiles than resident workgroups: each workgroup runs several
         // tiles in a row (the grid stays a multiple of the channel tiles)
         const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32) /
