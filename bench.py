@@ -108,6 +108,64 @@ def cpu_baseline(ci, cache_np, budget_s=12.0):
                        f"whole layer: {t_layer:.1f} s/layer")}
 
 
+def operand_probe(args):
+    """The workload's conv (same packed weights, scale and bias) timed on int8
+    inputs and caches drawn from different value distributions: the matrix
+    cores' throughput depends on the operand values (power), not only on the
+    instruction count.  Inputs are seeded draws; nothing is checked against the
+    oracle here (the kernels' parity is the tests' job)."""
+    import torch
+    from w8a8_int8_quantized_act_amd import ops
+    from w8a8_int8_quantized_act_amd import workloads as wl
+    dev = "cuda:0"
+    ci = wl.draw_workload(args.workload, only=args.level)[-1]
+    spec = ci.spec
+    kt = spec.k[0]
+    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev))
+    b = torch.from_numpy(ci.b).to(dev)
+    xs = torch.tensor([0.01], dtype=torch.float32, device=dev)
+    y = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev)
+    g = torch.Generator().manual_seed(11)
+    shape = (spec.N, spec.T, spec.H, spec.W, spec.Cin)
+    cshape = (spec.N, kt - 1, spec.H, spec.W, spec.Cin)
+
+    def codes(kind, shp):
+        if kind == "zero":
+            return torch.zeros(shp, dtype=torch.int8)
+        if kind == "small":
+            return torch.randint(-5, 6, shp, generator=g, dtype=torch.int8)
+        if kind == "silu":
+            z = torch.randn(shp, generator=g)
+            v = z * torch.sigmoid(z)
+            return torch.round(v / (v.abs().max() / 127)).clamp(-127, 127).to(torch.int8)
+        return torch.randint(-127, 128, shp, generator=g, dtype=torch.int8)
+
+    cnt = layer_counts(spec, True)
+    out = {"probe": "conv time by operand distribution", "workload": args.workload, "level": args.level,
+           "algorithmic_ops": cnt["ops"], "note": "input and 2-frame cache drawn from the same distribution; "
+           "median of 5 runs of 20 back-to-back launches (HIP events)", "results": {}}
+    stream = torch.cuda.current_stream()
+    for kind in ("zero", "small", "silu", "full"):
+        xq = codes(kind, shape).to(dev)
+        cache = codes(kind, cshape).to(dev) if kt > 1 else None
+        run = lambda: ops.causalconv3d_w8a8(xq, xs, wq, ws, b, cache, out=y)
+        for _ in range(3):
+            run()
+        torch.cuda.synchronize()
+        meds = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(20):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            meds.append(e0.elapsed_time(e1) / 20)
+        ms = sorted(meds)[2]
+        out["results"][kind] = {"conv_us": round(ms * 1e3, 2), "tops": round(cnt["ops"] / (ms * 1e-3) / 1e12, 1)}
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +177,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--operand-probe", action="store_true",
+                    help="only time the workload's conv on int8 inputs of different value distributions")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -130,6 +190,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
+
+    if args.operand_probe:
+        operand_probe(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
