@@ -91,8 +91,9 @@ int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh,
  *   x       bf16 bit patterns, numel elements (any layout)
  *   absmax  uint32 [QVAE_ABSMAX_WORDS], caller-allocated device buffer: this
  *           pass writes per-workgroup partial maxima of |x| (as bf16 bit
- *           patterns) into words 1.. ; qvae_act_quantize reduces them and
- *           stores the bf16 bit pattern of max |x| (0..0x7F7F) in word 0.
+ *           patterns) into words 1.. (all of them: 0 where no workgroup
+ *           reports); qvae_act_quantize reduces them and stores the bf16 bit
+ *           pattern of max |x| (0..0x7F7F) in word 0.
  * Inputs must be finite.  numel >= 1.  Pass the same x and numel to the
  * following qvae_act_quantize.
  */
@@ -103,7 +104,9 @@ int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax,
  * Activation quantization, second pass, with the scale derived on the device
  * from the partial maxima of qvae_act_absmax (fixed parameters: activation
  * clip ratio 1.0).
- *   absmax   in: partial maxima; out: word 0 = bf16 bit pattern of max |x|
+ *   absmax   in: partial maxima (from qvae_act_absmax on x, or from
+ *            qvae_causalconv3d_w8a8_absmax that produced x);
+ *            out: word 0 = bf16 bit pattern of max |x|
  *   x_scale  float32 [1] out: s = fl(clip * max |x|) / 127
  *   xq       int8 [numel] out: clamp(rne(x / s), -127, 127), 0 when s == 0
  * Supported: clip_ratio == 1.0f.
@@ -142,6 +145,26 @@ int qvae_causalconv3d_w8a8(const int8_t *xq, const float *x_scale,
                            const float *w_scale, const float *bias, int N,
                            int T, int H, int W, int Cin, int Cout, int kt,
                            int kh, int kw, uint16_t *y, void *stream);
+
+/*
+ * qvae_causalconv3d_w8a8 that also produces the activation maximum of its own
+ * output, for the next layer's quantizer (the absmax pass fused into the
+ * producing layer's epilogue):
+ *   y_absmax  uint32 [QVAE_ABSMAX_WORDS], caller-allocated device buffer, out:
+ *             words 1.. hold partial maxima of |y| over the output's pixels
+ *             inside the image (bf16 bit patterns), exactly as qvae_act_absmax
+ *             leaves them for y; word 0 is not touched.  Passing this buffer
+ *             and y to qvae_act_quantize quantizes y without its absmax pass.
+ * Same arguments, support and errors as qvae_causalconv3d_w8a8 otherwise;
+ * y_absmax == NULL is QVAE_EINVAL.
+ */
+int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_scale,
+                                  const int8_t *cache, const int8_t *wq,
+                                  const float *w_scale, const float *bias,
+                                  int N, int T, int H, int W, int Cin,
+                                  int Cout, int kt, int kh, int kw,
+                                  uint16_t *y, uint32_t *y_absmax,
+                                  void *stream);
 
 /*
  * Same contraction, writing the raw INT32 accumulators instead of the

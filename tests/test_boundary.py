@@ -33,7 +33,8 @@ def L():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["qvae_quantize_weights", "qvae_act_absmax", "qvae_act_quantize", "qvae_act_absmax_quant",
-              "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_acc32", "qvae_strerror", "qvae_version"]:
+              "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_absmax", "qvae_causalconv3d_w8a8_acc32",
+              "qvae_strerror", "qvae_version"]:
         assert n in names
 
 
@@ -81,6 +82,14 @@ def test_conv_rejects_unsupported(L):
     assert conv(L, dims=(1, 1, 4, 4, 32, 32, 3, 3, 1)) == -2      # kh != kw
     assert conv(L, dims=(1, 1, 4, 4, 32, 32, 3, 5, 5)) == -2      # 5x5
     assert conv(L, dims=(1, 1, 4, 4, 4960, 32, 3, 3, 3)) == -2    # 127^2 * K >= 2^31
+
+
+def test_conv_absmax_rejects(L):
+    f = L.qvae_causalconv3d_w8a8_absmax
+    dims = (1, 1, 4, 4, 32, 32, 3, 3, 3)
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, *dims, FAKE, None, None) == -1      # no maximum buffer
+    assert f(None, FAKE, None, FAKE, FAKE, None, *dims, FAKE, FAKE, None) == -1
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, 1, 1, 4, 4, 32, 40, 3, 3, 3, FAKE, FAKE, None) == -2
 
 
 def test_acc32_rejects(L):

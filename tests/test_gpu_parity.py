@@ -305,6 +305,49 @@ def test_conv_several_tiles_per_workgroup(ops, shape, cache_kind):
     assert ulp_dist(got_y, ref_y).max() == 0
 
 
+@pytest.mark.parametrize("shape,k,cache_kind", [
+    ((2, 64, 3, 11, 20), (3, 3, 3), "random"),   # ragged 8x16 / 16x16 tiles, cache
+    ((1, 96, 2, 33, 47), (3, 3, 3), None),       # 96-channel tiles (two workgroups per CU)
+    ((1, 384, 1, 40, 56), (3, 3, 3), "zero"),    # split K (few pixel tiles)
+    ((2, 384, 3, 60, 120), (3, 3, 3), None),     # several tiles per workgroup
+    ((1, 192, 2, 19, 23), (1, 1, 1), None),      # 1x1x1
+])
+def test_conv_output_absmax_feeds_the_next_quantize(ops, shape, k, cache_kind):
+    """The conv that also reports the partial maxima of its output: y is the
+    plain conv's bit for bit, word 0 after the next quantize pass is max |y|
+    over the output (out-of-image lanes excluded), and that pass quantizes y
+    exactly as the two-pass quantizer does."""
+    N, C, T, H, W = shape
+    ci = wl.draw_custom(90 + C + T, N, C, C, T, H, W, k=k)
+    kt = k[0]
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV))
+    _, xs_d, xq_d = ops.act_absmax_quant(to_dev_bits(ci.x))
+    b_d = torch.from_numpy(ci.b).to(DEV)
+    cache_d = None
+    if cache_kind == "zero":
+        cache_d = torch.zeros((N, kt - 1, H, W, C), dtype=torch.int8, device=DEV)
+    elif cache_kind == "random":
+        g = torch.Generator().manual_seed(3)
+        cache_d = torch.randint(-127, 128, (N, kt - 1, H, W, C), generator=g, dtype=torch.int8).to(DEV)
+    y_plain = ops.causalconv3d_w8a8(xq_d, xs_d, wq_d, ws_d, b_d, cache_d)
+    stale = torch.full((ops.ABSMAX_WORDS,), 0x7F7F, dtype=torch.int32, device=DEV)   # stale maxima everywhere
+    y, y_absmax = ops.causalconv3d_w8a8_absmax(xq_d, xs_d, wq_d, ws_d, b_d, cache_d, y_absmax=stale)
+    ys, yq = ops.act_quantize(y, y_absmax)
+    a2, ys2, yq2 = ops.act_absmax_quant(y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+    yb = bf16_bits(y)
+    true_max = int((yb & 0x7FFF).max())
+    assert int(y_absmax[0].item()) == true_max
+    assert int(a2[0].item()) == true_max
+    assert f32_bits(ys.item()) == f32_bits(ys2.item())
+    assert torch.equal(yq, yq2)
+    # and against the oracle's quantizer of y
+    a_o, s_o, q_o = oracle.act_absmax_quant(yb)
+    assert f32_bits(a_o) >> 16 == true_max and f32_bits(ys.item()) == f32_bits(s_o)
+    assert np.array_equal(yq.cpu().numpy(), q_o)
+
+
 def test_workload_single_96_t4_32_full(ops):
     ci = wl.draw_workload("single_96_t4_32")[0]
     r = _run_full_conv(ops, ci)

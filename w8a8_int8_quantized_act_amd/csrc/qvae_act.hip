@@ -16,8 +16,8 @@
 //                       workgroup writes its own partial maximum (no atomics:
 //                       hundreds of same-address atomics serialize in L2 and
 //                       cost more than the whole pass).
-//   pass 2  k_quantize  every workgroup reduces the <= 512 partials (2 KB from
-//                       L2), derives s, and quantizes: 16 bytes of bf16 in,
+//   pass 2  k_quantize  every workgroup reduces the 512 partial slots (2 KB
+//                       from L2; slots no producer owns are 0), derives s, and quantizes: 16 bytes of bf16 in,
 //                       8 int8 codes out per lane and load, four loads in
 //                       flight.  Workgroup 0 publishes the maximum and the
 //                       scale.
@@ -35,17 +35,9 @@ namespace qvae {
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Packed 2x16-bit unsigned max of the magnitudes held in one 32-bit word.
-__device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
-{
-    ushort2_t a = __builtin_bit_cast(ushort2_t, acc);
-    ushort2_t b = __builtin_bit_cast(ushort2_t, w & 0x7FFF7FFFu);
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
-}
-
 constexpr int kAbsmaxThreads = 1024;
 constexpr int kAbsmaxUnroll = 4;   // 16-byte loads in flight per lane
-constexpr int kAbsmaxParts = QVAE_ABSMAX_WORDS - 1;
+static_assert(kAbsmaxParts == QVAE_ABSMAX_WORDS - 1, "one word for the maximum, the rest partials");
 
 // Number of workgroups (= partial maxima) of the absmax pass for numel.
 static int absmax_blocks(int64_t numel)
@@ -100,6 +92,9 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
     __shared__ uint32_t part[kAbsmaxThreads / 64];
     const uint32_t b = block_max_u32(m, part);
     if (threadIdx.x == 0) partials[blockIdx.x] = b;
+    // every partial slot holds a valid maximum: the ones no workgroup owns are 0
+    if (blockIdx.x == 0)
+        for (int k = gridDim.x + threadIdx.x; k < kAbsmaxParts; k += kAbsmaxThreads) partials[k] = 0;
 }
 
 // One activation code by the definition: clamp(rne(fl(x / s)), -127, 127).
@@ -176,14 +171,14 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
                                                            int64_t numel,
                                                            float clip_ratio,
                                                            uint32_t *__restrict__ absmax,
-                                                           int nparts,
                                                            float *__restrict__ x_scale,
                                                            uint2 *__restrict__ q8,
                                                            int8_t *__restrict__ q)
 {
-    // the tensor's maximum from the absmax pass's partial maxima
+    // the tensor's maximum from all partial maxima (written by the absmax pass,
+    // or by the producing convolution's epilogue; unused slots are 0)
     uint32_t mp = 0;
-    for (int k = threadIdx.x; k < nparts; k += kQuantThreads) mp = max(mp, absmax[1 + k]);
+    for (int k = threadIdx.x; k < kAbsmaxParts; k += kQuantThreads) mp = max(mp, absmax[1 + k]);
     __shared__ uint32_t part[kQuantThreads / 64];
     const uint32_t mbits = block_max_u32(mp, part);
     const float a = bf16_bits_to_float(mbits);
@@ -247,8 +242,8 @@ extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ra
     const int64_t cap = (int64_t)device_cus() * 8;
     const int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
     hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, as_stream(stream),
-                       reinterpret_cast<const u32x4 *>(x), n16, x, numel, clip_ratio, absmax, absmax_blocks(numel),
-                       x_scale, reinterpret_cast<uint2 *>(xq), xq);
+                       reinterpret_cast<const u32x4 *>(x), n16, x, numel, clip_ratio, absmax, x_scale,
+                       reinterpret_cast<uint2 *>(xq), xq);
     return launch_status();
 }
 

@@ -77,6 +77,7 @@ struct ConvArgs {
     const int8_t *xq;
     const int8_t *cache;
     void *out;
+    uint32_t *y_absmax;     // partial-maximum slots of the output's |y|, or NULL
     int co_tiles, T, H, W, Cin, Cout, kt, N;
     int tiles_w, tiles_h;
 };
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // scalar loads and one wait, instead of a wait at each first use
     asm volatile("" ::"s"(a.wq), "s"(a.x_scale), "s"(a.w_scale), "s"(a.bias), "s"(a.xq), "s"(a.cache), "s"(a.out),
                  "s"(a.co_tiles), "s"(a.T), "s"(a.H), "s"(a.W), "s"(a.Cin), "s"(a.Cout), "s"(a.kt), "s"(a.N),
-                 "s"(a.tiles_w), "s"(a.tiles_h));
+                 "s"(a.tiles_w), "s"(a.tiles_h), "s"(a.y_absmax));
     // ---- tiles.  Pixel tiles are numbered pt = column + tiles_w * (row +
     // tiles_h * (t + T * n)).  Workgroup b runs channel tile b % co_tiles and
     // pixel tiles b / co_tiles + k * (gridDim.x / co_tiles), k = 0, 1, ...
@@ -443,6 +444,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // boundaries (the last stage of a tile prefetches the next tile's first
     // halo and weights), the epilogue of a tile runs while that halo waits in
     // its buffer.
+    uint32_t ymax = 0;   // packed running maximum of |y| (bf16 bits) over this lane's outputs
     auto epilogue = [&](const Tile &tl) __attribute__((always_inline)) {
         // ---- split K: each half finishes half of the pixel blocks.  Wave wk
         // exports to LDS the blocks the other half finishes; after the barrier it
@@ -508,10 +510,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         typedef float f4 __attribute__((ext_vector_type(4)));
         typedef float f2 __attribute__((ext_vector_type(2)));
         typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-        // this lane's per-channel factors and biases: read from LDS once when the
-        // wave tile is large (one wave per SIMD anyway, registers to spare after
-        // the K loop), else at each use so small tiles keep two waves per SIMD
-        constexpr bool HOIST = !ACC32 && MB * NB >= 12;
+        // this lane's per-channel factors and biases: read from LDS once with
+        // split K (one tile, registers to spare after the K loop), else at each
+        // use (a workgroup running several tiles carries its loop state through
+        // the epilogue, and small tiles keep two waves per SIMD)
+        constexpr bool HOIST = !ACC32 && WK > 1;
         f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
         if constexpr (HOIST) {
 #pragma unroll
@@ -527,6 +530,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         auto finish_block = [&](auto wkc, auto jc) {
             constexpr int WKC = decltype(wkc)::value;
             constexpr int j = decltype(jc)::value;
+            // the pixel this lane holds in the MFMA layout (row lrow of the block):
+            // only outputs inside the image count towards the output maximum
+            const int pl = (wpx * NB + WKC * HB + j) * 32 + lrow;
+            const int plr = pl / TW;
+            const bool px_in = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -548,10 +556,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                                 y[e] = __builtin_fmaf((float)v[e], s_fac[col], s_fac[C::BCO + col]);
                             }
                         }
-                        const bf2 lo = __builtin_convertvector(f2{y[0], y[1]}, bf2);
-                        const bf2 hi = __builtin_convertvector(f2{y[2], y[3]}, bf2);
-                        *reinterpret_cast<uint2 *>(dst) =
-                            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+                        const uint32_t lo =
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
+                        const uint32_t hi =
+                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                        if (px_in) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
                     }
                 }
 #pragma unroll
@@ -606,6 +616,25 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         epilogue(cur);
         break;
     }
+
+    // the workgroup's maximum of |y| into its partial slot (the output
+    // maximum the next layer's quantize pass reduces; slots 0..511, the grid
+    // has at most 512 workgroups when it is asked for)
+    if constexpr (!ACC32) {
+        if (a.y_absmax) {
+            __shared__ uint32_t s_red[NT / 64];
+            const uint32_t m = wave_max_u32(max(ymax & 0xFFFFu, ymax >> 16));
+            if (lane == 0) s_red[wave] = m;
+            lds_barrier();
+            if (tid == 0) {
+                uint32_t b = s_red[0];
+                for (int k = 1; k < NT / 64; ++k) b = max(b, s_red[k]);
+                a.y_absmax[blockIdx.x] = b;
+            }
+            if (blockIdx.x == 0)
+                for (int k = gridDim.x + tid; k < kAbsmaxParts; k += NT) a.y_absmax[k] = 0;
+        }
+    }
 }
 
 
@@ -647,7 +676,10 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
         const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32) /
                             a.co_tiles;
         if (per >= 1 && nptiles > per) grid = per * a.co_tiles;
+        // one partial slot per workgroup for the output maximum
+        if (a.y_absmax && grid > kAbsmaxParts) grid = (kAbsmaxParts / a.co_tiles) * a.co_tiles;
     }
+    if (a.y_absmax && (grid > kAbsmaxParts || grid < 1)) return QVAE_EUNSUPPORTED;
     if (acc32)
         hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>), dim3((unsigned)grid),
                            dim3(C::NT), 0, st, a);
@@ -744,6 +776,28 @@ extern "C" int qvae_causalconv3d_w8a8(const int8_t *xq, const float *x_scale, co
     a.w_scale = w_scale;
     a.bias = bias;
     a.out = y;
+    a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
+    return conv_dispatch(a, kh, false, as_stream(stream));
+}
+
+extern "C" int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_scale, const int8_t *cache,
+                                             const int8_t *wq, const float *w_scale, const float *bias, int N,
+                                             int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw,
+                                             uint16_t *y, uint32_t *y_absmax, void *stream)
+{
+    if (force_fail()) return QVAE_EFORCED;
+    if (!x_scale || !w_scale || !y_absmax) return QVAE_EINVAL;
+    int rc = conv_validate(xq, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
+    if (rc != QVAE_OK) return rc;
+    ConvArgs a{};
+    a.xq = xq;
+    a.cache = (kt > 1) ? cache : nullptr;
+    a.wq = wq;
+    a.x_scale = x_scale;
+    a.w_scale = w_scale;
+    a.bias = bias;
+    a.out = y;
+    a.y_absmax = y_absmax + 1;
     a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
     return conv_dispatch(a, kh, false, as_stream(stream));
 }

@@ -85,4 +85,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
     return max(max(r0, r1), max(r2, r3));
 }
 
+// Packed 2x16-bit unsigned max of the magnitudes held in one 32-bit word
+// (two bf16 bit patterns: for finite bf16, |a| < |b| iff (a & 0x7FFF) <
+// (b & 0x7FFF) as integers).
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
+{
+    typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+    const ushort2_t a = __builtin_bit_cast(ushort2_t, acc);
+    const ushort2_t b = __builtin_bit_cast(ushort2_t, w & 0x7FFF7FFFu);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+// Partial-maximum slots of an activation-maximum buffer (words 1.. of the
+// QVAE_ABSMAX_WORDS words): every producer writes all of them, 0 where it
+// has nothing, and the quantize pass reduces all of them.
+constexpr int kAbsmaxParts = 512;
+
 }  // namespace qvae

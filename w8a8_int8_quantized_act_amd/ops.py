@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.qvae_act_absmax_quant.restype = i32
         L.qvae_causalconv3d_w8a8.argtypes = [P, P, P, P, P, P] + [i32] * 9 + [P, P]
         L.qvae_causalconv3d_w8a8.restype = i32
+        L.qvae_causalconv3d_w8a8_absmax.argtypes = [P, P, P, P, P, P] + [i32] * 9 + [P, P, P]
+        L.qvae_causalconv3d_w8a8_absmax.restype = i32
         L.qvae_causalconv3d_w8a8_acc32.argtypes = [P, P, P] + [i32] * 9 + [P, P]
         L.qvae_causalconv3d_w8a8_acc32.restype = i32
         _lib = L
@@ -200,6 +202,31 @@ def causalconv3d_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor,
                                         N, T, H, W, Cin, Cout, kt, kh, kw, _p(out), _stream(stream)),
            "qvae_causalconv3d_w8a8")
     return out
+
+
+def causalconv3d_w8a8_absmax(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                             bias: torch.Tensor | None = None, cache: torch.Tensor | None = None,
+                             out: torch.Tensor | None = None, y_absmax: torch.Tensor | None = None, stream=None):
+    """causalconv3d_w8a8 that also leaves the partial maxima of |y| in an
+    activation-maximum buffer -> (y, y_absmax); act_quantize(y, y_absmax)
+    then quantizes y without its absmax pass."""
+    N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
+    _dev(x_scale, "x_scale", torch.float32)
+    _dev(w_scale, "w_scale", torch.float32)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+    if out is None:
+        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=xq.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (N, T, H, W, Cout):
+            raise ValueError("out shape")
+    if y_absmax is None:
+        y_absmax = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=xq.device)
+    _check(lib().qvae_causalconv3d_w8a8_absmax(_p(xq), _p(x_scale), _p(cache), _p(wq), _p(w_scale), _p(bias),
+                                               N, T, H, W, Cin, Cout, kt, kh, kw, _p(out), _p(y_absmax),
+                                               _stream(stream)), "qvae_causalconv3d_w8a8_absmax")
+    return out, y_absmax
 
 
 def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Tensor | None = None,
