@@ -108,6 +108,42 @@ def cpu_baseline(ci, cache_np, budget_s=12.0):
                        f"whole layer: {t_layer:.1f} s/layer")}
 
 
+def first_calls():
+    """First-call latency at each new resolution, in one process: every layer
+    of the two level sweeps (new shapes, new tile configurations) runs its
+    step (absmax + quantize + conv) once from a cold start at that shape, then
+    again; host wall clock around each call with a device synchronize on both
+    sides.  Nothing is compiled or tuned at run time: every kernel is built
+    ahead of time for gfx950."""
+    import numpy as np
+    import torch
+    from w8a8_int8_quantized_act_amd import ops
+    from w8a8_int8_quantized_act_amd import workloads as wl
+    dev = "cuda:0"
+    t0 = time.perf_counter()
+    ops.lib()
+    torch.zeros(1, device=dev)
+    torch.cuda.synchronize()
+    out = {"probe": "first call per resolution", "library_and_context_ms": round((time.perf_counter() - t0) * 1e3, 2),
+           "layers": []}
+    for key in ("sweep_1024", "sweep_840x1256"):
+        for ci in wl.draw_workload(key):
+            spec = ci.spec
+            x = torch.from_numpy(ci.x.view(np.int16)).to(dev).view(torch.bfloat16)
+            wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev))
+            b = torch.from_numpy(ci.b).to(dev)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(2):
+                t1 = time.perf_counter()
+                ops.layer_forward(x, wq, ws, b)
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t1) * 1e3)
+            out["layers"].append({"layer": f"{key} {spec.Cin}->{spec.Cout} @{spec.H}x{spec.W}",
+                                  "first_ms": round(ts[0], 3), "second_ms": round(ts[1], 3)})
+    print(json.dumps(out))
+
+
 def operand_probe(args):
     """The workload's conv (same packed weights, scale and bias) timed on int8
     inputs and caches drawn from different value distributions: the matrix
@@ -177,6 +213,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--first-calls", action="store_true",
+                    help="only time the first and second layer step at each resolution of the level sweeps")
     ap.add_argument("--operand-probe", action="store_true",
                     help="only time the workload's conv on int8 inputs of different value distributions")
     args = ap.parse_args()
@@ -194,6 +232,9 @@ def main():
 
     if args.operand_probe:
         operand_probe(args)
+        return
+    if args.first_calls:
+        first_calls()
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
