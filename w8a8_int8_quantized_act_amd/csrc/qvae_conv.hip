@@ -18,11 +18,13 @@
 // (B = activations, channels-last so K = Cin is contiguous per pixel),
 // K = valid temporal taps x kh x kw x Cin.  Nothing is materialised.
 //
-// Work split.  A workgroup owns a TH x TW pixel tile of one frame and BCO
-// output channels.  Each wave owns MB x NB blocks of 32x32 outputs
-// (MB*32 channels x NB*32 pixels) and, when WK = 2, half of the K range
-// (alternate 32-channel slices); the two K halves are summed through LDS
-// before the epilogue (INT32 sums are exact in any order).
+// Work split.  A workgroup owns BCO output channels and works through TH x TW
+// pixel tiles of one frame at a time (one tile, or several in a row when the
+// layer has more tiles than resident workgroups).  Each wave owns MB x NB
+// blocks of 32x32 outputs (MB*32 channels x NB*32 pixels) and, when WK = 2,
+// half of the K range (its own group of 32-channel slices in every stage);
+// the two K halves are summed through LDS before the epilogue (INT32 sums are
+// exact in any order).
 //
 // K loop.  A "stage" = one valid temporal tap i and SL 32-channel slices.
 // Per stage the workgroup stages in LDS only the activation halo
@@ -33,15 +35,18 @@
 // its own fragments straight from L2 into VGPRs, PD k-steps ahead of use.
 // Frames that are structurally zero (front padding without a cache) are
 // skipped, not multiplied.  Halo stages are double-buffered: the global loads
-// of stage s+1 are in flight while stage s computes.
+// of stage s+1 (of the next tile, after a tile's last stage) are in flight
+// while stage s computes.
 //
 // MFMA 32x32x32 i8 operands: lane L supplies 16 bytes of row/column (L % 32)
 // for K-half (L / 32); A and B use the same lane/byte -> k assignment, so the
 // product covers all 32 k of the slice whatever order the hardware sums them
 // in.  The INT32 result: lane L holds column L % 32 and, in register r, row
 // 8*(r/4) + 4*(L/32) + r%4 -- four consecutive output channels per register
-// quad, so the epilogue writes 4 bf16 (8 bytes) per store along the
-// channels-last output.
+// quad.  The epilogue rescales them and transposes each 32-pixel block
+// through LDS, so every lane stores 16 contiguous bytes of the channels-last
+// output; on request it also reduces the maximum of |y| into one partial slot
+// per workgroup (the next layer's activation maximum).
 #include <type_traits>
 #include <utility>
 
