@@ -35,7 +35,7 @@ namespace qvae {
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kAbsmaxThreads = 1024;
+constexpr int kAbsmaxThreads = 256;
 constexpr int kAbsmaxUnroll = 4;   // 16-byte loads in flight per lane
 static_assert(kAbsmaxParts == QVAE_ABSMAX_WORDS - 1, "one word for the maximum, the rest partials");
 
