@@ -141,7 +141,9 @@ struct ConvCfg {
     static constexpr int lds_bytes(int elem) { return work_bytes(elem) + FAC_BYTES; }
 };
 
-template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32>
+// ACC32: write the raw INT32 accumulators instead of the epilogue.  OUTMAX:
+// also reduce the maximum of |y| into a.y_absmax (one partial per workgroup).
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32, bool OUTMAX>
 __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 1) void k_conv_igemm(ConvArgs a)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
@@ -515,11 +517,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         typedef float f4 __attribute__((ext_vector_type(4)));
         typedef float f2 __attribute__((ext_vector_type(2)));
         typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-        // this lane's per-channel factors and biases: read from LDS once with
-        // split K (one tile, registers to spare after the K loop), else at each
-        // use (a workgroup running several tiles carries its loop state through
-        // the epilogue, and small tiles keep two waves per SIMD)
-        constexpr bool HOIST = !ACC32 && WK > 1;
+        // this lane's per-channel factors and biases: read from LDS once for the
+        // large wave tiles (registers to spare after the K loop), else at each
+        // use (small tiles keep two waves per SIMD; with the output maximum a
+        // workgroup running several tiles has no registers left for them)
+        constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
         f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
         if constexpr (HOIST) {
 #pragma unroll
@@ -537,9 +539,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             constexpr int j = decltype(jc)::value;
             // the pixel this lane holds in the MFMA layout (row lrow of the block):
             // only outputs inside the image count towards the output maximum
-            const int pl = (wpx * NB + WKC * HB + j) * 32 + lrow;
-            const int plr = pl / TW;
-            const bool px_in = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+            bool px_in = false;
+            if constexpr (OUTMAX) {
+                const int pl = (wpx * NB + WKC * HB + j) * 32 + lrow;
+                const int plr = pl / TW;
+                px_in = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+            }
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -566,7 +571,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                         const uint32_t hi =
                             __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
                         *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-                        if (px_in) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
+                        if constexpr (OUTMAX) {
+                            if (px_in) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
+                        }
                     }
                 }
 #pragma unroll
@@ -625,7 +632,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // the workgroup's maximum of |y| into its partial slot (the output
     // maximum the next layer's quantize pass reduces; slots 0..511, the grid
     // has at most 512 workgroups when it is asked for)
-    if constexpr (!ACC32) {
+    if constexpr (OUTMAX) {
         if (a.y_absmax) {
             __shared__ uint32_t s_red[NT / 64];
             const uint32_t m = wave_max_u32(max(ymax & 0xFFFFu, ymax >> 16));
@@ -648,15 +655,18 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
 // Workgroups of one instantiation that fit on a CU at once (registers, LDS,
 // waves), asked of the runtime once per instantiation.
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
-static int resident_per_cu(bool acc32)
+static int resident_per_cu(bool acc32, bool outmax)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
-    static int occ[2] = {0, 0};
-    int &o = occ[acc32 ? 1 : 0];
+    static int occ[3] = {0, 0, 0};
+    const int v = acc32 ? 1 : (outmax ? 2 : 0);
+    int &o = occ[v];
     if (o == 0) {
         int n = 0;
-        const void *f = acc32 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>)
-                              : reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>);
+        const void *f =
+            v == 1 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false>)
+            : v == 2 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true>)
+                     : reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false>);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, C::NT, 0) != hipSuccess || n < 1) n = 1;
         o = n;
     }
@@ -678,7 +688,7 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     if (WK == 1) {
         // more tiles than resident workgroups: each workgroup runs several
         // tiles in a row (the grid stays a multiple of the channel tiles)
-        const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32) /
+        const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32, a.y_absmax != nullptr) /
                             a.co_tiles;
         if (per >= 1 && nptiles > per) grid = per * a.co_tiles;
         // one partial slot per workgroup for the output maximum
@@ -686,10 +696,13 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     }
     if (a.y_absmax && (grid > kAbsmaxParts || grid < 1)) return QVAE_EUNSUPPORTED;
     if (acc32)
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false>), dim3((unsigned)grid),
+                           dim3(C::NT), 0, st, a);
+    else if (a.y_absmax)
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true>), dim3((unsigned)grid),
                            dim3(C::NT), 0, st, a);
     else
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false>), dim3((unsigned)grid),
+        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false>), dim3((unsigned)grid),
                            dim3(C::NT), 0, st, a);
     return launch_status();
 }
