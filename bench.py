@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -70,7 +71,7 @@ def read_traffic(workload_key, conv_src):
     return float(m_b.group(1))
 
 
-def cpu_baseline(ci, cache_np, budget_s=12.0):
+def cpu_baseline(ci, cache_np, budget_s=12.0, clip=1.0):
     """The CPU oracle (as it stands) on a bounded sample of the same layer:
     absmax + quantize over the whole input, the conv + epilogue over a random
     sample of output positions; scaled to the whole layer in TOPS."""
@@ -78,9 +79,9 @@ def cpu_baseline(ci, cache_np, budget_s=12.0):
     import oracle
 
     spec = ci.spec
-    wq, ws = oracle.quantize_weights(ci.w)
+    wq, ws = oracle.quantize_weights(ci.w, clip)
     t0 = time.perf_counter()
-    a, s, xq = oracle.act_absmax_quant(ci.x)
+    a, s, xq = oracle.act_absmax_quant(ci.x, clip)
     t_quant = time.perf_counter() - t0
     rng = np.random.default_rng(0)
     total = spec.positions
@@ -217,6 +218,10 @@ def main():
                     help="only time the first and second layer step at each resolution of the level sweeps")
     ap.add_argument("--operand-probe", action="store_true",
                     help="only time the workload's conv on int8 inputs of different value distributions")
+    ap.add_argument("--frames", type=int, default=0,
+                    help="a multi-frame variant: the layer's shape with T frames (redrawn, same recipe)")
+    ap.add_argument("--clip", type=float, default=1.0,
+                    help="activation and weight clip ratio in (0, 1] (the page fixes 1.0)")
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -255,13 +260,18 @@ def main():
     dev = "cuda:0"
 
     ci = wl.draw_workload(args.workload, only=args.level)[-1]
+    if args.frames and args.frames != ci.spec.T:
+        spec_t = dataclasses.replace(ci.spec, T=args.frames, name=f"{ci.spec.name}_t{args.frames}")
+        ci = wl.draw_conv(spec_t, torch.Generator().manual_seed(
+            1000 * wl.WORKLOADS[args.workload].seed + 10 * args.level + args.frames))
+    variant = ci.spec.T != wl.WORKLOADS[args.workload].convs[args.level].T or args.clip != 1.0
     spec = ci.spec
     kt = spec.k[0]
     use_cache = spec.zero_cache
     cnt = layer_counts(spec, use_cache)
 
     x = torch.from_numpy(ci.x.view(np.int16)).to(dev).view(torch.bfloat16)
-    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev))
+    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev), args.clip)
     b = torch.from_numpy(ci.b).to(dev)
     cache = (torch.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), dtype=torch.int8, device=dev)
              if use_cache else None)
@@ -278,7 +288,7 @@ def main():
     P = ctypes.c_void_p
     sp = P(stream.cuda_stream)
     a_absmax = (P(x.data_ptr()), x.numel(), P(absmax.data_ptr()), sp)
-    a_quant = (P(x.data_ptr()), x.numel(), ctypes.c_float(1.0), P(absmax.data_ptr()), P(xs.data_ptr()),
+    a_quant = (P(x.data_ptr()), x.numel(), ctypes.c_float(args.clip), P(absmax.data_ptr()), P(xs.data_ptr()),
                P(xq.data_ptr()), sp)
     a_conv = (P(xq.data_ptr()), P(xs.data_ptr()), P(cache.data_ptr()) if cache is not None else None,
               P(wq.data_ptr()), P(ws.data_ptr()), P(b.data_ptr()), spec.N, spec.T, spec.H, spec.W, spec.Cin,
@@ -390,7 +400,14 @@ def main():
     assert torch.equal(ref_y.view(torch.int16), y.view(torch.int16))
 
     conv_src = os.path.join(ROOT, "w8a8_int8_quantized_act_amd", "csrc", "qvae_conv.hip")
-    traffic = read_traffic(args.workload if args.level == 0 else f"{args.workload}_l{args.level}", conv_src)
+    traffic = None if variant else read_traffic(
+        args.workload if args.level == 0 else f"{args.workload}_l{args.level}", conv_src)
+    wl_name = (args.workload if args.level == 0 and len(wl.WORKLOADS[args.workload].convs) == 1
+               else f"{args.workload}[{args.level}]")
+    if ci.spec.T != wl.WORKLOADS[args.workload].convs[args.level].T:
+        wl_name += f" T={ci.spec.T}"
+    if args.clip != 1.0:
+        wl_name += f" clip={args.clip:g}"
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -405,8 +422,7 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {
-            "workload": args.workload if args.level == 0 and len(wl.WORKLOADS[args.workload].convs) == 1
-            else f"{args.workload}[{args.level}]",
+            "workload": wl_name,
             "layer": f"CausalConv3d {spec.k[0]}x{spec.k[1]}x{spec.k[2]} Cin={spec.Cin} Cout={spec.Cout} "
                      f"input [{spec.N},{spec.Cin},{spec.T},{spec.H},{spec.W}] bf16 channels-last"
                      + (", explicit 2-frame zero cache" if use_cache else ", causal front padding"),
@@ -456,7 +472,7 @@ def main():
     }
     if not args.no_cpu:
         cache_np = (np.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), np.int8) if use_cache else None)
-        out["cpu_baseline"] = cpu_baseline(ci, cache_np, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(ci, cache_np, args.cpu_budget, args.clip)
     print(json.dumps(out))
 
 

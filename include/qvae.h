@@ -73,8 +73,10 @@ const char *qvae_strerror(int status);
  *   w_scale  float32 [Cout]                   out
  * w_scale[co] = fl(clip * max |w[co,...]|) / 127, the maximum taken over
  * every (ci, kt, kh, kw); q = clamp(rne(w / w_scale[co]), -127, 127), 0 for
- * an all-zero channel.
- * Supported: clip_ratio == 1.0f, Cout % 32 == 0, Cin % 32 == 0,
+ * an all-zero channel.  The page fixes clip 1.0; a smaller ratio clips the
+ * channel's outliers to +-127.
+ * clip_ratio <= 0 or NaN is QVAE_EINVAL.
+ * Supported: 0 < clip_ratio <= 1, Cout % 32 == 0, Cin % 32 == 0,
  * kt, kh, kw in {1, 3}.
  */
 int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh,
@@ -103,20 +105,20 @@ int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax,
 /*
  * Activation quantization, second pass, with the scale derived on the device
  * from the partial maxima of qvae_act_absmax (fixed parameters: activation
- * clip ratio 1.0).
+ * clip ratio 1.0; a smaller ratio clips outliers to +-127).
  *   absmax   in: partial maxima (from qvae_act_absmax on x, or from
  *            qvae_causalconv3d_w8a8_absmax that produced x);
  *            out: word 0 = bf16 bit pattern of max |x|
  *   x_scale  float32 [1] out: s = fl(clip * max |x|) / 127
  *   xq       int8 [numel] out: clamp(rne(x / s), -127, 127), 0 when s == 0
- * Supported: clip_ratio == 1.0f.
+ * clip_ratio <= 0 or NaN is QVAE_EINVAL.  Supported: 0 < clip_ratio <= 1.
  */
 int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
                       uint32_t *absmax, float *x_scale, int8_t *xq,
                       void *stream);
 
 /* qvae_act_absmax followed by qvae_act_quantize on the same stream (two
- * launches, no host synchronization). */
+ * launches, no host synchronization); same clip_ratio rules. */
 int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
                           uint32_t *absmax, float *x_scale, int8_t *xq,
                           void *stream);

@@ -103,11 +103,16 @@ def test_quant_entry_points_reject(L):
     assert L.qvae_act_absmax(FAKE, 0, FAKE, None) == -1
     assert L.qvae_act_absmax(FAKE_MIS, 16, FAKE, None) == -1
     assert L.qvae_act_quantize(FAKE, 16, 1.0, None, FAKE, FAKE, None) == -1
-    assert L.qvae_act_quantize(FAKE, 16, 0.5, FAKE, FAKE, FAKE, None) == -2   # clip != 1
+    # clip ratio: (0, 1] is accepted; 0, negative and NaN are invalid, above 1 unsupported
+    nan = float("nan")
+    for clip, rc in [(0.0, -1), (-0.5, -1), (nan, -1), (1.5, -2), (float("inf"), -2)]:
+        assert L.qvae_act_quantize(FAKE, 16, clip, FAKE, FAKE, FAKE, None) == rc, clip
+        assert L.qvae_act_absmax_quant(FAKE, 16, clip, FAKE, FAKE, FAKE, None) == rc, clip
+        assert L.qvae_quantize_weights(FAKE, 32, 32, 3, 3, 3, clip, FAKE, FAKE, None) == rc, clip
     assert L.qvae_act_absmax_quant(FAKE, 16, 1.0, FAKE, FAKE, FAKE_MIS, None) == -1
-    assert L.qvae_act_absmax_quant(FAKE, 16, 0.9, FAKE, FAKE, FAKE, None) == -2
+    assert L.qvae_act_absmax_quant(FAKE, 16, 0.9, FAKE, FAKE, FAKE_MIS, None) == -1
     assert L.qvae_quantize_weights(None, 32, 32, 3, 3, 3, 1.0, FAKE, FAKE, None) == -1
-    assert L.qvae_quantize_weights(FAKE, 32, 32, 3, 3, 3, 0.5, FAKE, FAKE, None) == -2
+    assert L.qvae_quantize_weights(FAKE, 32, 32, 3, 3, 3, 0.5, FAKE_MIS, FAKE, None) == -1
     assert L.qvae_quantize_weights(FAKE, 32, 32, 2, 3, 3, 1.0, FAKE, FAKE, None) == -2
 
 

@@ -51,16 +51,17 @@ def f32_bits(v) -> int:
 
 
 # ------------------------------------------------------------------ activation quantization
-def _check_act(ops, x_bits):
+def _check_act(ops, x_bits, clip=1.0):
     xd = to_dev_bits(x_bits)
-    absmax_bits, x_scale, xq = ops.act_absmax_quant(xd)
+    absmax_bits, x_scale, xq = ops.act_absmax_quant(xd, clip)
     torch.cuda.synchronize()
-    a, s, q = oracle.act_absmax_quant(x_bits)
+    a, s, q = oracle.act_absmax_quant(x_bits, clip)
     assert int(absmax_bits[0].item()) == f32_bits(a) >> 16
     assert f32_bits(x_scale.item()) == f32_bits(s)
     got = xq.cpu().numpy()
     bad = np.count_nonzero(got != q)
     assert bad == 0, f"{bad} of {q.size} codes differ"
+    return q
 
 
 def _bits_of(x: torch.Tensor) -> np.ndarray:
@@ -119,6 +120,18 @@ def test_act_quant_zero_and_tiny(ops):
     _check_act(ops, _bits_of(big))
 
 
+@pytest.mark.parametrize("clip", [0.5, 0.9, 0.25, 1e-3])
+@pytest.mark.parametrize("n", [17, 4097, 1_000_003])
+def test_act_quant_clip_below_one(ops, clip, n):
+    # below clip 1 the scale shrinks and the clamp maps the tail to +-127
+    g = torch.Generator().manual_seed(105 + n % 89)
+    x = torch.randn(n, generator=g) * 3
+    m = torch.rand(x.shape, generator=g) < 0.05
+    q = _check_act(ops, _bits_of(torch.where(m, x * 20, x)), clip)
+    if n > 1000:
+        assert np.count_nonzero(np.abs(q.astype(np.int16)) == 127) > 1
+
+
 # ------------------------------------------------------------------ weight quantization
 @pytest.mark.parametrize("shape", [(384, 384, 3, 3, 3), (192, 384, 1, 1, 1), (96, 96, 3, 3, 3), (32, 64, 3, 1, 1)])
 def test_weight_quant_bitexact(ops, shape):
@@ -131,6 +144,20 @@ def test_weight_quant_bitexact(ops, shape):
     rq, rs = oracle.quantize_weights(w.numpy())
     assert np.array_equal(ws.cpu().numpy().view(np.uint32), rs.view(np.uint32))
     assert np.array_equal(wq.cpu().numpy(), pack_weight_codes(rq))
+
+
+@pytest.mark.parametrize("clip", [0.5, 0.9])
+@pytest.mark.parametrize("shape", [(384, 384, 3, 3, 3), (96, 96, 3, 3, 3), (192, 384, 1, 1, 1)])
+def test_weight_quant_clip_below_one(ops, shape, clip):
+    g = torch.Generator().manual_seed(210 + shape[0])
+    w = torch.randn(shape, generator=g) * 0.02
+    w[1] = 0.0
+    wq, ws = ops.quantize_weights(w.to(DEV), clip)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quantize_weights(w.numpy(), clip)
+    assert np.array_equal(ws.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(wq.cpu().numpy(), pack_weight_codes(rq))
+    assert np.count_nonzero(np.abs(rq.astype(np.int16)) == 127) > shape[0]
 
 
 # ------------------------------------------------------------------ the convolution, small shapes
@@ -347,6 +374,51 @@ def test_conv_output_absmax_feeds_the_next_quantize(ops, shape, k, cache_kind):
     a_o, s_o, q_o = oracle.act_absmax_quant(yb)
     assert f32_bits(a_o) >> 16 == true_max and f32_bits(ys.item()) == f32_bits(s_o)
     assert np.array_equal(yq.cpu().numpy(), q_o)
+
+
+@pytest.mark.parametrize("shape,cache_kind", [
+    ((1, 384, 2, 105, 157), None),          # latent level, odd sizes
+    ((1, 384, 2, 210, 314), "random"),      # second level, with a prev-frame cache
+    ((1, 192, 3, 420, 628), None),          # third level, three frames
+    ((1, 96, 2, 840, 1256), "random"),      # full-resolution level, with a cache
+], ids=["c384_105x157_t2", "c384_210x314_t2_cache", "c192_420x628_t3", "c96_840x1256_t2_cache"])
+def test_levels_multi_frame_clip_below_one(ops, shape, cache_kind):
+    """Every decoder level with several frames, activations quantized at clip 0.5
+    and weights at clip 0.9 (both clamps active), through the layer entry and the
+    conv that reports its output maximum, whose partial maxima then feed the next
+    layer's quantizer at clip 0.5; checked against the oracle on sampled positions."""
+    N, C, T, H, W = shape
+    clip_x, clip_w = 0.5, 0.9
+    ci = wl.draw_custom(400 + C + T, N, C, C, T, H, W, x_kind="silu")
+    cache = None
+    if cache_kind == "random":
+        cache = np.random.default_rng(9).integers(-127, 128, (N, 2, H, W, C)).astype(np.int8)
+    cache_d = None if cache is None else torch.from_numpy(cache).to(DEV)
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(ci.w).to(DEV), clip_w)
+    b_d = torch.from_numpy(ci.b).to(DEV)
+    x_d = to_dev_bits(ci.x)
+    y, xs_d, xq_d = ops.layer_forward(x_d, wq_d, ws_d, b_d, cache_d, clip_ratio=clip_x)
+    y2, y_absmax = ops.causalconv3d_w8a8_absmax(xq_d, xs_d, wq_d, ws_d, b_d, cache_d)
+    ys_d, yq_d = ops.act_quantize(y2, y_absmax, clip_x)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    wq, ws = oracle.quantize_weights(ci.w, clip_w)
+    assert np.array_equal(ws_d.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(wq_d.cpu().numpy(), pack_weight_codes(wq))
+    a, s, xq = oracle.act_absmax_quant(ci.x, clip_x)
+    assert f32_bits(xs_d.item()) == f32_bits(s)
+    got_xq = xq_d.cpu().numpy()
+    assert np.array_equal(got_xq, xq), f"{np.count_nonzero(got_xq != xq)} codes differ"
+    assert np.count_nonzero(np.abs(xq.astype(np.int16)) == 127) > 100        # the clamp fired
+    pos = sample_positions(N, T, H, W, 800, 11)
+    pos_d = torch.from_numpy(pos).to(DEV)
+    ref_y = oracle.epilogue(oracle.conv_acc(xq, wq, cache, positions=pos), s, ws, ci.b)
+    assert ulp_dist(bf16_bits(y.reshape(-1, C)[pos_d]), ref_y).max() == 0
+    # the next layer's quantizer on this output, from the fused partial maxima
+    yb = bf16_bits(y)
+    a2, s2, q2 = oracle.act_absmax_quant(yb, clip_x)
+    assert f32_bits(ys_d.item()) == f32_bits(s2)
+    assert np.array_equal(yq_d.cpu().numpy(), q2)
 
 
 def test_workload_single_96_t4_32_full(ops):

@@ -7,7 +7,8 @@ integer below 2^53), or a derived error bound against the unquantized float
 convolution.  The scheme being pinned is the one on the ComfyUI-Qwen-VAE-Triton
 v0.2.0 page, section "Three presets explained": symmetric per-output-channel
 INT8 weights, dynamic symmetric INT8 activations, INT32 accumulation, FP32
-rescale, output in the activation precision, clip ratio 1.0.
+rescale, output in the activation precision, clip ratio 1.0 (the page's
+fixed value; ratios below 1, where the clamp to +-127 fires, are pinned too).
 """
 import numpy as np
 import pytest
@@ -123,6 +124,36 @@ def test_act_quantize_all_zero(oracle):
     assert a == 0 and s == 0 and not q.any()
 
 
+@pytest.mark.parametrize("clip,min_clamped", [(0.5, 500), (0.9, 5)])
+def test_act_quantize_clip_below_one(oracle, clip, min_clamped):
+    # a clip ratio below 1 shrinks the scale; the clamp maps the clipped tail to +-127
+    g = torch.Generator().manual_seed(14)
+    x = (torch.randn(50000, generator=g) * 3).to(torch.bfloat16)
+    xb = x.view(torch.int16).numpy().view(np.uint16)
+    a, s, q = oracle.act_absmax_quant(xb, clip)
+    assert a == oracle.act_absmax(xb)
+    assert s == np.float32(np.float32(clip) * np.float32(a)) / np.float32(127)
+    assert s < oracle.scale_from_absmax(a)
+    xf = f32(xb).astype(np.float64)
+    qi = q.astype(int)
+    # numpy's float32 division and rint (half to even), then the clamp
+    ref = np.clip(np.rint(f32(xb) / np.float32(s)), -127, 127).astype(np.int8)
+    assert np.array_equal(q, ref)
+    # beyond 128 steps the code is +-127 with the sign of x, and the clamp really fires
+    far = np.abs(xf) >= 128.0 * float(s)
+    assert far.sum() >= min_clamped
+    assert np.all(qi[far] == np.where(xf[far] > 0, 127, -127))
+    # inside the clip range the usual half-step error bound holds
+    inside = np.abs(xf) <= 127.0 * float(s)
+    err = np.abs(xf[inside] - qi[inside] * float(s))
+    assert np.all(err <= float(s) * (0.5 + 2.0 ** -17))
+    # odd symmetry and monotonicity survive the clamp
+    qn = oracle.act_quantize(xb ^ np.uint16(0x8000), s)
+    assert np.array_equal(qn.astype(int), -qi)
+    order = np.argsort(xf, kind="stable")
+    assert np.all(np.diff(qi[order]) >= 0)
+
+
 # --------------------------------------------------------------- weight quantization
 def test_weight_quant_per_channel_closed_form(oracle):
     w = np.zeros((3, 2, 3, 3, 3), np.float32)
@@ -153,6 +184,36 @@ def test_weight_quant_matches_numpy(oracle):
     assert np.array_equal(wq, q_ref.transpose(0, 2, 3, 4, 1))
     # each channel's extreme weight maps to +-127
     assert np.all(np.abs(wq.reshape(32, -1).astype(int)).max(axis=1) == 127)
+
+
+def test_weight_quant_clip_half_closed_form(oracle):
+    # max 2.0 and clip 0.5: s = fl(1.0 / 127); weights at or beyond 1.0 clamp to +-127
+    w = np.zeros((2, 32, 1, 1, 1), np.float32)
+    w[0, :6, 0, 0, 0] = [2.0, -1.0, 1.5, 0.25, -0.125, 10.0 / 127.0]
+    w[1, 3, 0, 0, 0] = -4.0
+    w[1, 4, 0, 0, 0] = 1.0
+    wq, s_w = oracle.quantize_weights(w, 0.5)
+    assert s_w[0] == np.float32(1.0) / np.float32(127)
+    assert s_w[1] == np.float32(2.0) / np.float32(127)
+    assert wq[0, 0, 0, 0, :6].tolist() == [127, -127, 127, 32, -16, 10]
+    # 1.0 / fl(2/127) rounds to exactly 63.5 in binary32: a tie, which goes to the even code
+    assert wq[1, 0, 0, 0, 3] == -127 and wq[1, 0, 0, 0, 4] == 64
+    assert np.count_nonzero(wq) == 8
+
+
+@pytest.mark.parametrize("clip", [0.5, 0.9])
+def test_weight_quant_clip_matches_numpy(oracle, clip):
+    g = torch.Generator().manual_seed(15)
+    w = (torch.randn(32, 16, 3, 3, 3, generator=g) * 0.02).numpy()
+    wq, s_w = oracle.quantize_weights(w, clip)
+    a = np.abs(w).reshape(32, -1).max(axis=1).astype(np.float32)
+    s_ref = ((np.float32(clip) * a).astype(np.float32) / np.float32(127)).astype(np.float32)
+    assert np.array_equal(s_w, s_ref)
+    q_ref = np.clip(np.rint(w / s_ref[:, None, None, None, None]), -127, 127).astype(np.int8)
+    assert np.array_equal(wq, q_ref.transpose(0, 2, 3, 4, 1))
+    # every channel has clamped weights at these ratios (randn's tail beyond clip * max)
+    clamped = (np.abs(wq.reshape(32, -1).astype(int)) == 127).sum(axis=1)
+    assert np.all(clamped >= 1)
 
 
 # --------------------------------------------------------------- the INT32 contraction
@@ -416,3 +477,23 @@ def test_quantized_conv_within_derived_bound(oracle, x_kind, x_scale):
     assert ratio.max() <= 1.0
     # and the typical error is far inside the worst case (random rounding errors)
     assert np.sqrt(np.mean((y - y_ref) ** 2)) < 0.2 * np.sqrt(np.mean(bound ** 2))
+
+
+def test_layer_clip_below_one_bruteforce(oracle):
+    """The whole layer at clip 0.5 against numpy quantization + the pure-Python
+    convolution + the (separately pinned) epilogue."""
+    g = torch.Generator().manual_seed(16)
+    N, T, H, W, Cin, Cout = 1, 2, 3, 4, 32, 32
+    xb = (torch.randn(N, T, H, W, Cin, generator=g) * 2).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    w = (torch.randn(Cout, Cin, 3, 3, 3, generator=g) * 0.05).numpy()
+    b = (torch.randn(Cout, generator=g) * 0.1).numpy()
+    wq, s_w = oracle.quantize_weights(w, 0.5)
+    y, s_x = oracle.layer(xb, wq, s_w, b, clip_ratio=0.5)
+    xf = f32(xb)
+    a = np.abs(xf).max()
+    s_ref = np.float32(np.float32(0.5) * a) / np.float32(127)
+    assert s_x == s_ref
+    xq = np.clip(np.rint(xf / s_ref), -127, 127).astype(np.int8)
+    assert np.count_nonzero(np.abs(xq.astype(int)) == 127) > 10
+    acc = np.array(conv_acc_bruteforce(xq.astype(int).tolist(), wq.astype(int).tolist()), np.int32)
+    assert np.array_equal(y, oracle.epilogue(acc, s_x, s_w, b))

@@ -2,8 +2,9 @@
 //
 // Scheme (page "ComfyUI-Qwen-VAE-Triton v0.2.0", section "Three presets
 // explained"): activations are dynamically, symmetrically quantized to INT8
-// with clip ratio 1.0.  One scale per tensor: s = fl(absmax) / 127 and
-// q = clamp(rne(x / s), -127, 127).
+// with clip ratio 1.0.  One scale per tensor: s = fl(clip * absmax) / 127 and
+// q = clamp(rne(x / s), -127, 127).  Any clip ratio in (0, 1] is accepted;
+// below 1 the clamp is what maps the clipped outliers to +-127.
 //
 // Two HBM-bound passes.  The scale is a grid-wide dependency, so the max is
 // reduced first (pass 1) and every quantize workgroup derives the same scale
@@ -234,7 +235,8 @@ extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ra
     if (force_fail()) return QVAE_EFORCED;
     if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
-    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN
+    if (clip_ratio > 1.0f) return QVAE_EUNSUPPORTED;
     const int64_t n16 = numel / 8;
     // enough workgroups for every lane to have kQuantUnroll loads in flight,
     // at most 8 per CU (one grid-stride sweep of the tensor per unrolled pass)
@@ -253,7 +255,8 @@ extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float cli
     if (force_fail()) return QVAE_EFORCED;
     if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
-    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN
+    if (clip_ratio > 1.0f) return QVAE_EUNSUPPORTED;
     int rc = qvae_act_absmax(x, numel, absmax, stream);
     if (rc != QVAE_OK) return rc;
     return qvae_act_quantize(x, numel, clip_ratio, absmax, x_scale, xq, stream);

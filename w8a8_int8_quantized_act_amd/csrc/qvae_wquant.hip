@@ -2,8 +2,9 @@
 //
 // Scheme (page "ComfyUI-Qwen-VAE-Triton v0.2.0", section "Three presets
 // explained"): symmetric INT8 weights, one scale per output channel, weight
-// clip ratio 1.0.  s[co] = fl(max |w[co,...]|) / 127 over every
+// clip ratio 1.0.  s[co] = fl(clip * max |w[co,...]|) / 127 over every
 // (ci, kt, kh, kw) of the channel; q = clamp(rne(w / s[co]), -127, 127).
+// Any clip ratio in (0, 1] is accepted.
 //
 // Runs once per layer at load time.  One workgroup per output channel: a
 // max-reduction over the channel (non-negative floats compare like their bit
@@ -81,7 +82,8 @@ extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, 
     if (force_fail()) return QVAE_EFORCED;
     if (!w || !wq || !w_scale || Cout <= 0 || Cin <= 0 || kt <= 0 || kh <= 0 || kw <= 0)
         return QVAE_EINVAL;
-    if (clip_ratio != 1.0f) return QVAE_EUNSUPPORTED;
+    if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN
+    if (clip_ratio > 1.0f) return QVAE_EUNSUPPORTED;
     if ((kt != 1 && kt != 3) || (kh != 1 && kh != 3) || (kw != 1 && kw != 3)) return QVAE_EUNSUPPORTED;
     if (Cout % 32 != 0 || Cin % 32 != 0) return QVAE_EUNSUPPORTED;
     if (!aligned16(wq)) return QVAE_EINVAL;

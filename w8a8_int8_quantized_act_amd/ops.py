@@ -241,10 +241,10 @@ def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Ten
 
 
 def layer_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, bias: torch.Tensor | None = None,
-                  cache: torch.Tensor | None = None, stream=None):
+                  cache: torch.Tensor | None = None, clip_ratio: float = 1.0, stream=None):
     """One W8A8 CausalConv3d layer: absmax -> quantize -> implicit-GEMM conv.
 
     x bf16 [N][T][H][W][Cin] -> (y bf16 [N][T][H][W][Cout], x_scale, xq)."""
-    _, x_scale, xq = act_absmax_quant(x, stream=stream)
+    _, x_scale, xq = act_absmax_quant(x, clip_ratio, stream=stream)
     y = causalconv3d_w8a8(xq, x_scale, wq, w_scale, bias, cache, stream=stream)
     return y, x_scale, xq
