@@ -33,8 +33,10 @@
  *     aborts or throws; on a non-zero status the caller is expected to fall
  *     back to its native-precision path;
  *   - setting the environment variable QVAE_FORCE_FAIL=1 makes every call
- *     return QVAE_EFORCED without launching anything (to exercise the
- *     caller's fallback);
+ *     that launches work return QVAE_EFORCED without launching anything;
+ *     QVAE_FORCE_FAIL=w8a8 does so only for the W8A8 calls (the quantizers
+ *     and the INT8 convolutions), so a caller's per-layer fallback to the
+ *     native-precision convolution runs instead (the page's "disable" A/B);
  *   - concurrent calls on different streams are safe as long as their output
  *     buffers do not alias.
  */
@@ -167,6 +169,69 @@ int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_scale,
                                   int Cout, int kt, int kh, int kw,
                                   uint16_t *y, uint32_t *y_absmax,
                                   void *stream);
+
+/*
+ * Layer selection (section "Three presets explained": the patch covers 28
+ * Conv3d layers of the decoder; Conservative quantizes the highest channel
+ * level, 15 layers; Balanced the two highest levels, 22, keeping the 96-channel
+ * level native; Aggressive every eligible layer, 26, except the two the fixed
+ * rule keeps native, decoder.upsamples.14.residual.2 and .6).
+ */
+#define QVAE_PRESET_NATIVE 0        /* no layer quantized                     */
+#define QVAE_PRESET_CONSERVATIVE 1
+#define QVAE_PRESET_BALANCED 2
+#define QVAE_PRESET_AGGRESSIVE 3
+
+/*
+ * 1 if the preset runs the named Conv3d layer in W8A8, 0 if it keeps it in
+ * native precision, QVAE_EINVAL for a NULL name, a non-positive size or an
+ * unknown preset.  Host only (no device work, never forced to fail).
+ *   name          the layer's module name, e.g. "decoder.middle.0.residual.2"
+ *                 (any prefix before "decoder." is allowed)
+ *   Cin, Cout, kt, kh, kw   the layer's shape
+ *   top_channels  the decoder's widest channel count (384 for the Wan /
+ *                 Qwen-Image VAE)
+ * Eligible: a decoder residual-block conv (name ending in ".residual.2" or
+ * ".residual.6") of 3x3x3 with Cin and Cout multiples of 32.  Conservative:
+ * eligible with Cin = Cout = top_channels.  Balanced: eligible with Cin and
+ * Cout >= top_channels / 2.  Aggressive: eligible.  The two excluded layers are
+ * native under every preset.
+ */
+int qvae_select_layer(int preset, const char *name, int Cin, int Cout, int kt, int kh, int kw,
+                      int top_channels);
+
+/*
+ * Native-precision weights for the layers left unquantized: a permutation of
+ * the bf16 weights into the order the convolution's matrix-core loop reads.
+ *   w   bf16 bit patterns [Cout][Cin][kt][kh][kw]
+ *   wp  bf16 bit patterns, Cout*Cin*kt*kh*kw values, out, 16-byte aligned:
+ *         wp[cb][i][s][j*kw + l][L][e] = w(co = 32*cb + L%32,
+ *                                          ci = 16*s + 8*(L/32) + e, i, j, l)
+ *       for cb < Cout/32, s < Cin/16, L < 64, e < 8 (1 KB per fragment of 32
+ *       output x 16 input channels)
+ * Supported: Cout % 32 == 0, Cin % 16 == 0, kt, kh, kw in {1, 3}.
+ */
+int qvae_pack_weights_bf16(const uint16_t *w, int Cout, int Cin, int kt, int kh, int kw, uint16_t *wp,
+                           void *stream);
+
+/*
+ * Native-precision causal 3-D convolution (the layers a preset keeps in the
+ * VAE's own precision): bf16 x bf16 products, FP32 accumulation,
+ *   y[n,t,h,w,co] = bf16_rne(fl32(sum over (i, j, l, ci) of w * X) + bias[co])
+ * with X, the frame rules and the padding of qvae_causalconv3d_w8a8; the FP32
+ * sum is formed in the matrix cores' order (not a fixed sequential order).
+ *   x      bf16 bit patterns [N][T][H][W][Cin]
+ *   cache  bf16 bit patterns [N][kt-1][H][W][Cin] (the kt-1 frames before
+ *          frame 0, oldest first) or NULL = zero front frames
+ *   wp     from qvae_pack_weights_bf16
+ *   bias   float32 [Cout] or NULL (zero)
+ *   y      bf16 bit patterns [N][T][H][W][Cout] out
+ * Supported: Cin % 16 == 0, Cout % 32 == 0, kt in {1, 3}, (kh, kw) in
+ * {(1, 1), (3, 3)}.
+ */
+int qvae_causalconv3d_bf16(const uint16_t *x, const uint16_t *cache, const uint16_t *wp, const float *bias,
+                           int N, int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw, uint16_t *y,
+                           void *stream);
 
 /*
  * Same contraction, writing the raw INT32 accumulators instead of the

@@ -75,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_layer.argtypes = ([P, P, P, P, P] + [i32] * 9 +
                                    [f32, P, i64, P, P, P, P])
         L.oracle_layer.restype = i32
+        L.oracle_conv_bf16_positions.argtypes = [P, P, P, P] + [i32] * 9 + [P, i64, P, P]
+        L.oracle_conv_bf16_positions.restype = i32
         _lib = L
     return _lib
 
@@ -226,3 +228,37 @@ def layer(x_bf16_bits, wq, s_w, bias, cache=None, positions=None, clip_ratio=1.0
     if rc != OK:
         raise ValueError(f"oracle layer failed: {rc}")
     return y, np.float32(sx.value)
+
+
+# ---------------------------------------------------------------- native-precision conv
+def conv_bf16(x_bf16_bits, w_bf16_bits, bias=None, cache=None, positions=None):
+    """bf16 conv of the layers a preset leaves unquantized.
+
+    x uint16 bf16 bits [N][T][H][W][Cin]; w uint16 bf16 bits
+    [Cout][Cin][kt][kh][kw]; bias float32 [Cout] or None; cache uint16
+    [N][kt-1][H][W][Cin] or None.  Returns (z, mag), float64 of shape
+    [npos][Cout] (or [N][T][H][W][Cout] without ``positions``): z the exact
+    value (before any rounding to bf16), mag the sum of |x w| plus |bias|."""
+    x = _c(x_bf16_bits, np.uint16)
+    w = _c(w_bf16_bits, np.uint16)
+    N, T, H, W, Cin = x.shape
+    Cout, Cin2, kt, kh, kw = w.shape
+    if Cin2 != Cin:
+        raise ValueError("Cin mismatch")
+    b = None if bias is None else _c(bias, np.float32)
+    if cache is not None:
+        cache = _c(cache, np.uint16)
+        if cache.shape != (N, kt - 1, H, W, Cin):
+            raise ValueError(f"cache shape {cache.shape}")
+    if positions is None:
+        npos, pos, shape = N * T * H * W, None, (N, T, H, W, Cout)
+    else:
+        pos = _c(np.asarray(positions, np.int64), np.int64)
+        npos, shape = pos.size, (pos.size, Cout)
+    z = np.empty(shape, np.float64)
+    mag = np.empty(shape, np.float64)
+    rc = lib().oracle_conv_bf16_positions(_ptr(x), _ptr(cache), _ptr(w), _ptr(b), N, T, H, W, Cin, Cout,
+                                          kt, kh, kw, _ptr(pos), npos, _ptr(z), _ptr(mag))
+    if rc != OK:
+        raise ValueError(f"oracle bf16 conv failed: {rc}")
+    return z, mag

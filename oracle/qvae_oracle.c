@@ -16,7 +16,9 @@
  *     symmetric INT8 activations, INT8 x INT8 products accumulated in INT32,
  *     an FP32 rescale, and output kept in the activation's precision;
  *   - same section, fixed-parameter paragraph: activation clip ratio 1.0,
- *     weight clip ratio 1.0, channels_last layout.
+ *     weight clip ratio 1.0, channels_last layout;
+ *   - same section, the presets: the layers a preset leaves out keep the
+ *     VAE's native precision (here a bf16 convolution, computed exactly).
  * The page leaves open the activation-scale granularity, rounding, clamp range,
  * division form, epilogue order and the causal padding; the readings taken
  * here (per-tensor absmax/127, round-half-to-even, clamp to +-127, IEEE
@@ -273,6 +275,79 @@ void oracle_epilogue_f32(const int32_t *acc, int64_t npos, int Cout, float s_x,
             float b = bias ? bias[co] : 0.0f;
             y32[p * Cout + co] = fmaf(a, m, b);
         }
+}
+
+/* ---- native-precision conv, for the layers a preset leaves unquantized ----
+ * Same preset section of the page: the layers outside the chosen set keep
+ * the VAE's own precision.  x bf16 [N][T][H][W][Cin], cache bf16
+ * [N][kt-1][H][W][Cin] or NULL, w bf16 [Cout][Cin][kt][kh][kw] (the usual
+ * Conv3d weight layout), bias float32 [Cout] or NULL.  For each listed output
+ * position and channel:
+ *   z   = sum over (i, j, l, ci) of x * w, plus bias   (the exact value: each
+ *         product of two bf16 numbers is exact in binary64, and the binary64
+ *         sum of K products is within K * 2^-53 of the exact sum)
+ *   mag = sum of |x * w|, plus |bias|                 (scales the rounding
+ *         error a float32 accumulation may make)
+ * Frame and padding rules are those of the INT8 convolution above. */
+int oracle_conv_bf16_positions(const uint16_t *x, const uint16_t *cache,
+                               const uint16_t *w, const float *bias, int N,
+                               int T, int H, int W, int Cin, int Cout, int kt,
+                               int kh, int kw, const int64_t *pos, int64_t npos,
+                               double *z, double *mag)
+{
+    if (!x || !w || !z || !mag || N <= 0 || T <= 0 || H <= 0 || W <= 0 ||
+        Cin <= 0 || Cout <= 0 || kt <= 0 || kh <= 0 || kw <= 0 || npos < 0)
+        return ORACLE_EARG;
+    const int64_t total = (int64_t)N * T * H * W;
+    const int ph = (kh - 1) / 2, pw = (kw - 1) / 2;
+    int status = ORACLE_OK;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t p = 0; p < npos; ++p) {
+        int64_t q = pos ? pos[p] : p;
+        if (q < 0 || q >= total) {
+#pragma omp atomic write
+            status = ORACLE_EARG;
+            continue;
+        }
+        int wo = (int)(q % W);
+        int h = (int)((q / W) % H);
+        int t = (int)((q / ((int64_t)W * H)) % T);
+        int n = (int)(q / ((int64_t)W * H * T));
+        for (int co = 0; co < Cout; ++co) {
+            double sum = 0.0, abs_sum = 0.0;
+            for (int i = 0; i < kt; ++i) {
+                int tau = t - (kt - 1) + i;
+                const uint16_t *frame;
+                if (tau >= 0) {
+                    frame = x + ((int64_t)n * T + tau) * H * W * Cin;
+                } else if (cache) {
+                    frame = cache + ((int64_t)n * (kt - 1) + (kt - 1 + tau)) * H * W * Cin;
+                } else {
+                    continue;             /* zero front padding              */
+                }
+                for (int j = 0; j < kh; ++j) {
+                    int hh = h - ph + j;
+                    if (hh < 0 || hh >= H) continue;
+                    for (int l = 0; l < kw; ++l) {
+                        int ww = wo - pw + l;
+                        if (ww < 0 || ww >= W) continue;
+                        const uint16_t *xp = frame + ((int64_t)hh * W + ww) * Cin;
+                        for (int ci = 0; ci < Cin; ++ci) {
+                            int64_t widx = ((((int64_t)co * Cin + ci) * kt + i) * kh + j) * kw + l;
+                            double prod = (double)oracle_bf16_to_f32(xp[ci]) *
+                                          (double)oracle_bf16_to_f32(w[widx]);
+                            sum += prod;
+                            abs_sum += fabs(prod);
+                        }
+                    }
+                }
+            }
+            double b = bias ? (double)bias[co] : 0.0;
+            z[p * Cout + co] = sum + b;
+            mag[p * Cout + co] = abs_sum + fabs(b);
+        }
+    }
+    return status;
 }
 
 /* ---- the whole layer, end to end (used for CPU timing) -------------------

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["qvae_quantize_weights", "qvae_act_absmax", "qvae_act_quantize", "qvae_act_absmax_quant",
               "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_absmax", "qvae_causalconv3d_w8a8_acc32",
+              "qvae_select_layer", "qvae_pack_weights_bf16", "qvae_causalconv3d_bf16",
               "qvae_strerror", "qvae_version"]:
         assert n in names
 
@@ -116,6 +117,26 @@ def test_quant_entry_points_reject(L):
     assert L.qvae_quantize_weights(FAKE, 32, 32, 2, 3, 3, 1.0, FAKE, FAKE, None) == -2
 
 
+def test_bf16_entry_points_reject(L):
+    f = L.qvae_causalconv3d_bf16
+    dims = (1, 1, 4, 4, 32, 32, 3, 3, 3)
+    assert f(None, None, FAKE, None, *dims, FAKE, None) == -1
+    assert f(FAKE, None, None, None, *dims, FAKE, None) == -1
+    assert f(FAKE, None, FAKE, None, *dims, None, None) == -1
+    assert f(FAKE_MIS, None, FAKE, None, *dims, FAKE, None) == -1
+    assert f(FAKE, FAKE_MIS, FAKE, None, *dims, FAKE, None) == -1
+    assert f(FAKE, None, FAKE, None, 1, 1, 4, 4, 24, 32, 3, 3, 3, FAKE, None) == -2    # Cin % 16
+    assert f(FAKE, None, FAKE, None, 1, 1, 4, 4, 32, 48, 3, 3, 3, FAKE, None) == -2    # Cout % 32
+    assert f(FAKE, None, FAKE, None, 1, 1, 4, 4, 32, 32, 2, 3, 3, FAKE, None) == -2    # kt = 2
+    assert f(FAKE, None, FAKE, None, 1, 1, 4, 4, 32, 32, 3, 1, 3, FAKE, None) == -2    # kh != kw
+    p = L.qvae_pack_weights_bf16
+    assert p(None, 32, 32, 3, 3, 3, FAKE, None) == -1
+    assert p(FAKE, 32, 32, 3, 3, 3, FAKE_MIS, None) == -1
+    assert p(FAKE, 32, 0, 3, 3, 3, FAKE, None) == -1
+    assert p(FAKE, 40, 32, 3, 3, 3, FAKE, None) == -2
+    assert p(FAKE, 32, 24, 3, 3, 3, FAKE, None) == -2
+
+
 def test_force_fail_hook():
     # QVAE_FORCE_FAIL=1: every call returns QVAE_EFORCED before any launch
     code = (
@@ -130,6 +151,27 @@ def test_force_fail_hook():
         "     L.qvae_causalconv3d_w8a8_acc32(F, None, F, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None)]\n"
         "sys.exit(0 if r == [-4] * 6 else 1)\n")
     env = dict(os.environ, QVAE_FORCE_FAIL="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_force_fail_w8a8_only():
+    # QVAE_FORCE_FAIL=w8a8: the W8A8 calls fail, the native-precision calls still
+    # validate their arguments (the fake pointers are rejected as usual, not forced)
+    code = (
+        "import ctypes, sys\n"
+        "from w8a8_int8_quantized_act_amd import ops\n"
+        "L = ops.lib(); F = ctypes.c_void_p(0x10000); M = ctypes.c_void_p(0x10008)\n"
+        "w8 = [L.qvae_act_absmax(F, 16, F, None),\n"
+        "      L.qvae_act_quantize(F, 16, 1.0, F, F, F, None),\n"
+        "      L.qvae_quantize_weights(F, 32, 32, 3, 3, 3, 1.0, F, F, None),\n"
+        "      L.qvae_causalconv3d_w8a8(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
+        "      L.qvae_causalconv3d_w8a8_absmax(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, F, None)]\n"
+        "nat = [L.qvae_causalconv3d_bf16(M, None, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
+        "       L.qvae_pack_weights_bf16(F, 32, 32, 3, 3, 3, M, None)]\n"
+        "sel = L.qvae_select_layer(3, b'decoder.middle.0.residual.2', 384, 384, 3, 3, 3, 384)\n"
+        "sys.exit(0 if w8 == [-4] * 5 and nat == [-1, -1] and sel == 1 else 1)\n")
+    env = dict(os.environ, QVAE_FORCE_FAIL="w8a8")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
 

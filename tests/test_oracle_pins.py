@@ -497,3 +497,69 @@ def test_layer_clip_below_one_bruteforce(oracle):
     assert np.count_nonzero(np.abs(xq.astype(int)) == 127) > 10
     acc = np.array(conv_acc_bruteforce(xq.astype(int).tolist(), wq.astype(int).tolist()), np.int32)
     assert np.array_equal(y, oracle.epilogue(acc, s_x, s_w, b))
+
+
+# --------------------------------------------------------------- native-precision conv (bf16)
+def _bf16_bits_of(t):
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_bf16_conv_integer_values_bruteforce(oracle, with_cache):
+    # small integers are exact in bf16, so the exact conv is the integer conv
+    g = torch.Generator().manual_seed(31)
+    N, T, H, W, Cin, Cout = 1, 3, 4, 5, 3, 4
+    xi = torch.randint(-9, 10, (N, T, H, W, Cin), generator=g)
+    wi = torch.randint(-9, 10, (Cout, Cin, 3, 3, 3), generator=g)
+    ci = torch.randint(-9, 10, (N, 2, H, W, Cin), generator=g) if with_cache else None
+    z, mag = oracle.conv_bf16(_bf16_bits_of(xi.float()), _bf16_bits_of(wi.float()), None,
+                              None if ci is None else _bf16_bits_of(ci.float()))
+    w_cl = wi.permute(0, 2, 3, 4, 1).tolist()          # [Cout][kt][kh][kw][Cin] for the brute force
+    ref = conv_acc_bruteforce(xi.tolist(), w_cl, None if ci is None else ci.tolist())
+    assert np.array_equal(z, np.array(ref, np.float64))
+    ref_abs = conv_acc_bruteforce(xi.abs().tolist(), wi.abs().permute(0, 2, 3, 4, 1).tolist(),
+                                  None if ci is None else ci.abs().tolist())
+    assert np.array_equal(mag, np.array(ref_abs, np.float64))
+
+
+@pytest.mark.parametrize("k,with_cache", [((3, 3, 3), False), ((3, 3, 3), True), ((1, 1, 1), False),
+                                          ((3, 1, 1), True), ((1, 3, 3), False)])
+def test_bf16_conv_matches_f64_library_conv(oracle, k, with_cache):
+    g = torch.Generator().manual_seed(32)
+    N, T, H, W, Cin, Cout = 2, 3, 7, 9, 16, 32
+    kt, kh, kw = k
+    x = _bf16_bits_of(torch.randn(N, T, H, W, Cin, generator=g) * 2)
+    w = _bf16_bits_of(torch.randn(Cout, Cin, kt, kh, kw, generator=g) * 0.1)
+    b = (torch.randn(Cout, generator=g) * 0.1).numpy()
+    cache = _bf16_bits_of(torch.randn(N, kt - 1, H, W, Cin, generator=g)) if with_cache else None
+    z, mag = oracle.conv_bf16(x, w, b, cache)
+    xt = torch.from_numpy(f32(x).astype(np.float64)).permute(0, 4, 1, 2, 3)
+    if cache is not None:
+        xt = torch.cat([torch.from_numpy(f32(cache).astype(np.float64)).permute(0, 4, 1, 2, 3), xt], dim=2)
+    else:
+        xt = F.pad(xt, (0, 0, 0, 0, kt - 1, 0))
+    xt = F.pad(xt, ((kw - 1) // 2, (kw - 1) // 2, (kh - 1) // 2, (kh - 1) // 2, 0, 0))
+    wt = torch.from_numpy(f32(w).astype(np.float64))
+    ref = F.conv3d(xt, wt, torch.from_numpy(b.astype(np.float64))).permute(0, 2, 3, 4, 1).numpy()
+    assert np.all(np.abs(z - ref) <= 1e-12 * mag + 1e-300)
+    ref_mag = F.conv3d(xt.abs(), wt.abs(), torch.from_numpy(np.abs(b).astype(np.float64)))
+    assert np.allclose(mag, ref_mag.permute(0, 2, 3, 4, 1).numpy(), rtol=1e-12, atol=0)
+
+
+def test_bf16_conv_zero_cache_and_causality(oracle):
+    g = torch.Generator().manual_seed(33)
+    N, T, H, W, Cin, Cout = 1, 4, 5, 6, 16, 32
+    x = _bf16_bits_of(torch.randn(N, T, H, W, Cin, generator=g))
+    w = _bf16_bits_of(torch.randn(Cout, Cin, 3, 3, 3, generator=g) * 0.1)
+    z0, _ = oracle.conv_bf16(x, w)
+    zc, _ = oracle.conv_bf16(x, w, cache=np.zeros((N, 2, H, W, Cin), np.uint16))
+    assert np.array_equal(z0, zc)
+    x2 = x.copy()
+    x2[:, 2:] = _bf16_bits_of(torch.randn(N, T - 2, H, W, Cin, generator=g))    # change frames 2, 3
+    z2, _ = oracle.conv_bf16(x2, w)
+    assert np.array_equal(z0[:, :2], z2[:, :2])                                 # frames 0, 1 unchanged
+    assert not np.array_equal(z0[:, 2:], z2[:, 2:])
+    # positions give the same values as the full tensor
+    pos = np.array([0, 7, 29, N * T * H * W - 1])
+    zp, _ = oracle.conv_bf16(x, w, positions=pos)
+    assert np.array_equal(zp, z0.reshape(-1, Cout)[pos])

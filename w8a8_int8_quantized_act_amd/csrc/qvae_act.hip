@@ -219,7 +219,7 @@ using namespace qvae;
 
 extern "C" int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absmax, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!x || !absmax || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x)) return QVAE_EINVAL;
     const int64_t n16 = numel / 8;
@@ -232,7 +232,7 @@ extern "C" int qvae_act_absmax(const uint16_t *x, int64_t numel, uint32_t *absma
 extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio, uint32_t *absmax,
                                  float *x_scale, int8_t *xq, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
     if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN
@@ -252,7 +252,7 @@ extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ra
 extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio, uint32_t *absmax,
                                      float *x_scale, int8_t *xq, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!x || !absmax || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
     if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
     if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN

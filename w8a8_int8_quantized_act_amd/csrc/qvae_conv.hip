@@ -56,7 +56,16 @@ namespace qvae {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// What a launch computes (one kernel instantiation each):
+//   kModePlain  W8A8, bf16 output (with the output maximum when y_absmax is set)
+//   kModeAcc32  W8A8, raw INT32 accumulators
+//   kModeBf16   bf16 x bf16 products, FP32 accumulation, y = bf16_rne(acc + bias)
+//               (the native-precision conv for the layers left unquantized)
+constexpr int kModePlain = 0, kModeAcc32 = 1, kModeBf16 = 2;
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): the index
 // is a compile-time constant in every call, so arrays it selects from stay in
@@ -143,9 +152,16 @@ struct ConvCfg {
 
 // ACC32: write the raw INT32 accumulators instead of the epilogue.  OUTMAX:
 // also reduce the maximum of |y| into a.y_absmax (one partial per workgroup).
-template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32, bool OUTMAX>
+// BF: bf16 operands (the kernel moves bytes: a.Cin is the bytes per pixel,
+// 2 x the channels, so a 32-byte slice holds 16 channels and one 16-byte lane
+// fragment feeds the bf16 matrix instruction exactly as it feeds the INT8
+// one), FP32 accumulators, y = bf16_rne(fma(acc, 1, bias)).
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32, bool OUTMAX,
+          bool BF>
 __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 1) void k_conv_igemm(ConvArgs a)
 {
+    static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
+    using AccV = std::conditional_t<BF, v16f, v16i>;
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     constexpr int NT = C::NT;
     constexpr int PH = (KH - 1) / 2, PW = (KW - 1) / 2;
@@ -244,14 +260,14 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     float f_ws[FPT], f_b[FPT];
     float sx = 0.0f;
     if constexpr (!ACC32) {
-        sx = *a.x_scale;
+        sx = BF ? 1.0f : *a.x_scale;
 #pragma unroll
         for (int k = 0; k < FPT; ++k) {
             const int c = tid + k * NT;
             f_ws[k] = 0.0f;
             f_b[k] = 0.0f;
             if (c < C::BCO) {
-                f_ws[k] = a.w_scale[co0 + c];
+                f_ws[k] = BF ? 1.0f : a.w_scale[co0 + c];
                 if (a.bias) f_b[k] = a.bias[co0 + c];
             }
         }
@@ -339,11 +355,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + lhalf * 16 + wk * C::SPW * C::SLICE_BYTES;
     }
 
-    v16i acc[MB][NB];
+    AccV acc[MB][NB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = AccV{};
 
     store_halo(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -412,7 +428,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                 for (int nb = 0; nb < NB; ++nb) {
                     constexpr int last = MB * NB - 1;
                     const int i = mb * NB + nb;
-                    acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+                    if constexpr (BF)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wreg[slot][mb]),
+                                                                              __builtin_bit_cast(bf16x8_t, bcur[nb]),
+                                                                              acc[mb][nb], 0, 0, 0);
+                    else
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
                     if (i < NB && e + 1 < C::KS) bnext[i] = read_b1(xs, e + 1, i);
 #pragma unroll
@@ -456,7 +477,8 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         // ---- split K: each half finishes half of the pixel blocks.  Wave wk
         // exports to LDS the blocks the other half finishes; after the barrier it
         // reads the other half's export of its own blocks into registers and adds
-        // it while rescaling (INT32 sums, exact in any order).
+        // it while rescaling (INT32 sums, exact in any order; FP32 sums of the
+        // bf16 conv add the same two partials whichever wave finishes).
         constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
         v4i part[(WK > 1) ? MB * HB * 4 : 1];
         if constexpr (WK > 1) {
@@ -467,7 +489,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                 static_for<MB>([&](auto mbc) {
                     static_for<HB>([&](auto jc) {
                         constexpr int mb = decltype(mbc)::value, j = decltype(jc)::value;
-                        const v16i v = acc[mb][other * HB + j];
+                        const v16i v = __builtin_bit_cast(v16i, acc[mb][other * HB + j]);
 #pragma unroll
                         for (int g = 0; g < 4; ++g)
                             exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
@@ -549,9 +571,15 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const v16i &x = acc[mb][WKC * HB + j];
+                    const v16i x = __builtin_bit_cast(v16i, acc[mb][WKC * HB + j]);
                     v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-                    if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                    f4 vf{};
+                    if constexpr (BF) {
+                        vf = __builtin_bit_cast(f4, v);
+                        if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[(mb * HB + j) * 4 + g]);
+                    } else {
+                        if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                    }
                     char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
                     if constexpr (ACC32) {
                         *reinterpret_cast<v4i *>(dst) = v;
@@ -559,11 +587,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                         f4 y;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
+                            const float av = BF ? vf[e] : (float)v[e];
                             if constexpr (HOIST) {
-                                y[e] = __builtin_fmaf((float)v[e], fm[mb][g][e], fb[mb][g][e]);
+                                y[e] = __builtin_fmaf(av, fm[mb][g][e], fb[mb][g][e]);
                             } else {
                                 const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
-                                y[e] = __builtin_fmaf((float)v[e], s_fac[col], s_fac[C::BCO + col]);
+                                y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
                             }
                         }
                         const uint32_t lo =
@@ -613,7 +642,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = v16i{};
+                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = AccV{};
                 if constexpr (PERSIST == 1) {
                     wcur = wstage(cur, 0);
 #pragma unroll
@@ -652,21 +681,32 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
 
 // ---- host side ------------------------------------------------------------
 
+// The kernel instantiation of one launch mode (the output maximum is a mode
+// of its own only for the W8A8 epilogue).
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
+static const void *conv_kernel(int mode, bool outmax)
+{
+    if (mode == kModeAcc32)
+        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false, false>);
+    if (mode == kModeBf16)
+        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, true>);
+    if (outmax)
+        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true, false>);
+    return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, false>);
+}
+
 // Workgroups of one instantiation that fit on a CU at once (registers, LDS,
 // waves), asked of the runtime once per instantiation.
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
-static int resident_per_cu(bool acc32, bool outmax)
+static int resident_per_cu(int mode, bool outmax)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
-    static int occ[3] = {0, 0, 0};
-    const int v = acc32 ? 1 : (outmax ? 2 : 0);
+    static int occ[4] = {0, 0, 0, 0};
+    const int v = (mode == kModePlain && outmax) ? 3 : mode;
     int &o = occ[v];
     if (o == 0) {
         int n = 0;
-        const void *f =
-            v == 1 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false>)
-            : v == 2 ? reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true>)
-                     : reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false>);
+        const void *f = conv_kernel<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(mode, outmax);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, C::NT, 0) != hipSuccess || n < 1) n = 1;
         o = n;
     }
@@ -674,7 +714,7 @@ static int resident_per_cu(bool acc32, bool outmax)
 }
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
-static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
+static int launch_cfg(const ConvArgs &base, int mode, hipStream_t st)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     ConvArgs a = base;
@@ -684,26 +724,21 @@ static int launch_cfg(const ConvArgs &base, bool acc32, hipStream_t st)
     a.co_tiles = a.Cout / C::BCO;
     const int64_t nptiles = (int64_t)a.tiles_w * a.tiles_h * a.T * a.N;
     if (nptiles * a.co_tiles > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
+    const bool outmax = a.y_absmax != nullptr;
     int64_t grid = nptiles * a.co_tiles;
     if (WK == 1) {
         // more tiles than resident workgroups: each workgroup runs several
         // tiles in a row (the grid stays a multiple of the channel tiles)
-        const int64_t per = (int64_t)device_cus() * resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(acc32, a.y_absmax != nullptr) /
-                            a.co_tiles;
+        const int64_t per = (int64_t)device_cus() *
+                            resident_per_cu<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(mode, outmax) / a.co_tiles;
         if (per >= 1 && nptiles > per) grid = per * a.co_tiles;
         // one partial slot per workgroup for the output maximum
-        if (a.y_absmax && grid > kAbsmaxParts) grid = (kAbsmaxParts / a.co_tiles) * a.co_tiles;
+        if (outmax && grid > kAbsmaxParts) grid = (kAbsmaxParts / a.co_tiles) * a.co_tiles;
     }
-    if (a.y_absmax && (grid > kAbsmaxParts || grid < 1)) return QVAE_EUNSUPPORTED;
-    if (acc32)
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false>), dim3((unsigned)grid),
-                           dim3(C::NT), 0, st, a);
-    else if (a.y_absmax)
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true>), dim3((unsigned)grid),
-                           dim3(C::NT), 0, st, a);
-    else
-        hipLaunchKernelGGL((k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false>), dim3((unsigned)grid),
-                           dim3(C::NT), 0, st, a);
+    if (outmax && (grid > kAbsmaxParts || grid < 1)) return QVAE_EUNSUPPORTED;
+    const void *f = conv_kernel<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(mode, outmax);
+    void *args[] = {&a};
+    (void)hipLaunchKernel(f, dim3((unsigned)grid), dim3(C::NT), args, 0, st);   // a failure is reported below
     return launch_status();
 }
 
@@ -718,59 +753,69 @@ static int64_t px_tiles(const ConvArgs &a, int th, int tw)
 // workgroup.  1x1 kernels stage two slices per wave per stage when the slice
 // count allows it, so a stage still holds more than one k-step.
 template <int KH, int KW, int SPW>
-static int launch_spatial(const ConvArgs &a, bool acc32, hipStream_t st)
+static int launch_spatial(const ConvArgs &a, int mode, hipStream_t st)
 {
     const int64_t cus = device_cus();
     const int S = a.Cin / 32;
     const bool k2 = S % (2 * SPW) == 0;   // the K range splits into two equal halves
     if (a.Cout % 96 == 0) {
         if (a.Cout % 384 == 0 && (px_tiles(a, 8, 16) * (a.Cout / 384) >= cus || !k2))
-            return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+            return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
         if (a.Cout % 192 == 0 && (px_tiles(a, 16, 16) * (a.Cout / 192) >= cus || !k2))
-            return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
-        if (a.Cout % 192 == 0) return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+            return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
+        if (a.Cout % 192 == 0) return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
         if constexpr (KH * KW > 1) {
             // 96 channels: memory-bound; 96x64 wave tiles keep two workgroups
             // per CU so one's loads and stores overlap the other's MFMAs
             if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
-                return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, acc32, st);
+                return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, mode, st);
         } else {
             if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
-                return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
+                return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
         }
-        return launch_cfg<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, acc32, st);
+        return launch_cfg<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
     }
-    return launch_cfg<1, 2, 1, 1, 4, 16, 16, KH, KW, SPW>(a, acc32, st);
+    return launch_cfg<1, 2, 1, 1, 4, 16, 16, KH, KW, SPW>(a, mode, st);
 }
 
-static int conv_validate(const int8_t *xq, const int8_t *wq, const void *out, int N, int T, int H, int W,
-                         int Cin, int Cout, int kt, int kh, int kw, const int8_t *cache)
+// Shape checks shared by both operand types; cin_bytes = bytes per input
+// pixel (Cin for int8, 2 Cin for bf16), out_elem = bytes per output value.
+static int conv_validate(const void *x, const void *w, const void *out, int N, int T, int H, int W, int Cin,
+                         int Cout, int kt, int kh, int kw, const void *cache, int64_t cin_bytes, int out_elem)
 {
-    if (!xq || !wq || !out) return QVAE_EINVAL;
+    if (!x || !w || !out) return QVAE_EINVAL;
     if (N <= 0 || T <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || kt <= 0 || kh <= 0 || kw <= 0)
         return QVAE_EINVAL;
-    if (!aligned16(xq) || !aligned16(wq) || !aligned16(out) || (cache && !aligned16(cache))) return QVAE_EINVAL;
-    if (Cin % 32 != 0 || Cout % 32 != 0) return QVAE_EUNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || !aligned16(out) || (cache && !aligned16(cache))) return QVAE_EINVAL;
+    if (cin_bytes % 32 != 0 || Cout % 32 != 0) return QVAE_EUNSUPPORTED;
     if (kt != 1 && kt != 3) return QVAE_EUNSUPPORTED;
     if (!((kh == 1 && kw == 1) || (kh == 3 && kw == 3))) return QVAE_EUNSUPPORTED;
-    // |acc| <= 127^2 * K must stay inside int32
-    const int64_t K = (int64_t)Cin * kt * kh * kw;
-    if (K * 127 * 127 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
     // byte offsets inside one frame are 32-bit
-    if ((int64_t)H * W * Cin >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
-    // output byte offsets inside one pixel tile (at most 32 rows, INT32 export) are 32-bit
-    if ((int64_t)32 * W * Cout * 4 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
+    if ((int64_t)H * W * cin_bytes >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
+    // output byte offsets inside one pixel tile (at most 32 rows) are 32-bit
+    if ((int64_t)32 * W * Cout * out_elem >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
     return QVAE_OK;
 }
 
-static int conv_dispatch(const ConvArgs &a, int kh, bool acc32, hipStream_t st)
+static int conv_validate_w8a8(const int8_t *xq, const int8_t *wq, const void *out, int N, int T, int H, int W,
+                              int Cin, int Cout, int kt, int kh, int kw, const int8_t *cache)
 {
-    // two 32-channel slices per wave and stage when the slice count is even:
+    int rc = conv_validate(xq, wq, out, N, T, H, W, Cin, Cout, kt, kh, kw, cache, Cin, 4);
+    if (rc != QVAE_OK) return rc;
+    // |acc| <= 127^2 * K must stay inside int32
+    const int64_t K = (int64_t)Cin * kt * kh * kw;
+    if (K * 127 * 127 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
+    return QVAE_OK;
+}
+
+static int conv_dispatch(const ConvArgs &a, int kh, int mode, hipStream_t st)
+{
+    // two 32-byte slices per wave and stage when the slice count is even:
     // half the stages (barriers) and 64 contiguous bytes per halo pixel load
-    if (kh == 3 && (a.Cin / 32) % 2 == 0) return launch_spatial<3, 3, 2>(a, acc32, st);
-    if (kh == 3) return launch_spatial<3, 3, 1>(a, acc32, st);
-    if ((a.Cin / 32) % 2 == 0) return launch_spatial<1, 1, 2>(a, acc32, st);
-    return launch_spatial<1, 1, 1>(a, acc32, st);
+    if (kh == 3 && (a.Cin / 32) % 2 == 0) return launch_spatial<3, 3, 2>(a, mode, st);
+    if (kh == 3) return launch_spatial<3, 3, 1>(a, mode, st);
+    if ((a.Cin / 32) % 2 == 0) return launch_spatial<1, 1, 2>(a, mode, st);
+    return launch_spatial<1, 1, 1>(a, mode, st);
 }
 
 }  // namespace qvae
@@ -782,9 +827,9 @@ extern "C" int qvae_causalconv3d_w8a8(const int8_t *xq, const float *x_scale, co
                                       int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw,
                                       uint16_t *y, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!x_scale || !w_scale) return QVAE_EINVAL;
-    int rc = conv_validate(xq, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
+    int rc = conv_validate_w8a8(xq, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
     if (rc != QVAE_OK) return rc;
     ConvArgs a{};
     a.xq = xq;
@@ -795,7 +840,7 @@ extern "C" int qvae_causalconv3d_w8a8(const int8_t *xq, const float *x_scale, co
     a.bias = bias;
     a.out = y;
     a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
-    return conv_dispatch(a, kh, false, as_stream(stream));
+    return conv_dispatch(a, kh, kModePlain, as_stream(stream));
 }
 
 extern "C" int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_scale, const int8_t *cache,
@@ -803,9 +848,9 @@ extern "C" int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_sc
                                              int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw,
                                              uint16_t *y, uint32_t *y_absmax, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!x_scale || !w_scale || !y_absmax) return QVAE_EINVAL;
-    int rc = conv_validate(xq, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
+    int rc = conv_validate_w8a8(xq, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
     if (rc != QVAE_OK) return rc;
     ConvArgs a{};
     a.xq = xq;
@@ -817,15 +862,15 @@ extern "C" int qvae_causalconv3d_w8a8_absmax(const int8_t *xq, const float *x_sc
     a.out = y;
     a.y_absmax = y_absmax + 1;
     a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
-    return conv_dispatch(a, kh, false, as_stream(stream));
+    return conv_dispatch(a, kh, kModePlain, as_stream(stream));
 }
 
 extern "C" int qvae_causalconv3d_w8a8_acc32(const int8_t *xq, const int8_t *cache, const int8_t *wq, int N,
                                             int T, int H, int W, int Cin, int Cout, int kt, int kh, int kw,
                                             int32_t *acc, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
-    int rc = conv_validate(xq, wq, acc, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
+    if (force_fail(true)) return QVAE_EFORCED;
+    int rc = conv_validate_w8a8(xq, wq, acc, N, T, H, W, Cin, Cout, kt, kh, kw, cache);
     if (rc != QVAE_OK) return rc;
     ConvArgs a{};
     a.xq = xq;
@@ -833,5 +878,22 @@ extern "C" int qvae_causalconv3d_w8a8_acc32(const int8_t *xq, const int8_t *cach
     a.wq = wq;
     a.out = acc;
     a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
-    return conv_dispatch(a, kh, true, as_stream(stream));
+    return conv_dispatch(a, kh, kModeAcc32, as_stream(stream));
+}
+
+extern "C" int qvae_causalconv3d_bf16(const uint16_t *x, const uint16_t *cache, const uint16_t *wp,
+                                      const float *bias, int N, int T, int H, int W, int Cin, int Cout, int kt,
+                                      int kh, int kw, uint16_t *y, void *stream)
+{
+    if (force_fail(false)) return QVAE_EFORCED;
+    int rc = conv_validate(x, wp, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache, 2 * (int64_t)Cin, 2);
+    if (rc != QVAE_OK) return rc;
+    ConvArgs a{};
+    a.xq = reinterpret_cast<const int8_t *>(x);
+    a.cache = (kt > 1) ? reinterpret_cast<const int8_t *>(cache) : nullptr;
+    a.wq = reinterpret_cast<const int8_t *>(wp);
+    a.bias = bias;
+    a.out = y;
+    a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = 2 * Cin, a.Cout = Cout, a.kt = kt;
+    return conv_dispatch(a, kh, kModeBf16, as_stream(stream));
 }

@@ -9,11 +9,16 @@
 
 namespace qvae {
 
-// Every entry point starts with this: the fallback test hook, then nothing.
-inline bool force_fail()
+// Every entry point starts with this: the fallback test hook.
+// QVAE_FORCE_FAIL=1 fails every call; QVAE_FORCE_FAIL=w8a8 fails only the
+// W8A8 calls (quantizers and the INT8 conv), so a caller's per-layer fallback
+// to the native-precision conv runs instead.
+inline bool force_fail(bool w8a8)
 {
     const char *v = getenv("QVAE_FORCE_FAIL");
-    return v && v[0] == '1';
+    if (!v) return false;
+    if (v[0] == '1' && v[1] == 0) return true;
+    return w8a8 && v[0] == 'w' && v[1] == '8' && v[2] == 'a' && v[3] == '8' && v[4] == 0;
 }
 
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }

@@ -72,14 +72,56 @@ __global__ __launch_bounds__(kWqThreads) void k_quantize_weights(const float *__
     }
 }
 
+// Native-precision weights for the layers left unquantized: bf16 values in
+// the same fragment order, a fragment holding 32 output x 16 input channels
+// (one kilobyte, 16 bytes per lane):
+//   wp[co/32][i][ci/16][j*kw + l][lane][e],  lane = 32*((ci%16)/8) + co%32,
+//   e = ci % 8.
+// One thread per weight, a pure permutation (no arithmetic).
+__global__ __launch_bounds__(kWqThreads) void k_pack_weights_bf16(const uint16_t *__restrict__ w, int Cin, int kt,
+                                                                  int kh, int kw, int64_t total,
+                                                                  uint16_t *__restrict__ wp)
+{
+    const int64_t e = (int64_t)blockIdx.x * kWqThreads + threadIdx.x;
+    if (e >= total) return;
+    const int taps = kt * kh * kw, khw = kh * kw;
+    const int64_t per_co = (int64_t)Cin * taps;
+    const int co = (int)(e / per_co);
+    const int64_t r = e - (int64_t)co * per_co;
+    const int ci = (int)(r / taps);
+    const int tap = (int)(r - (int64_t)ci * taps);
+    const int i = tap / khw, sp = tap - i * khw;
+    const int S = Cin >> 4;
+    const int cb = co >> 5, row = co & 31;
+    const int sl = ci >> 4, c = ci & 15;
+    const int lane = (c >> 3) * 32 + row;
+    const int64_t dst = ((((int64_t)cb * kt + i) * S + sl) * khw + sp) * 512 + lane * 8 + (c & 7);
+    wp[dst] = w[e];
+}
+
 }  // namespace qvae
 
 using namespace qvae;
 
+extern "C" int qvae_pack_weights_bf16(const uint16_t *w, int Cout, int Cin, int kt, int kh, int kw, uint16_t *wp,
+                                      void *stream)
+{
+    if (force_fail(false)) return QVAE_EFORCED;
+    if (!w || !wp || Cout <= 0 || Cin <= 0 || kt <= 0 || kh <= 0 || kw <= 0) return QVAE_EINVAL;
+    if ((kt != 1 && kt != 3) || (kh != 1 && kh != 3) || (kw != 1 && kw != 3)) return QVAE_EUNSUPPORTED;
+    if (Cout % 32 != 0 || Cin % 16 != 0) return QVAE_EUNSUPPORTED;
+    if (!aligned16(wp)) return QVAE_EINVAL;
+    const int64_t total = (int64_t)Cout * Cin * kt * kh * kw;
+    if ((total + kWqThreads - 1) / kWqThreads > 0x7FFFFFFF) return QVAE_EUNSUPPORTED;
+    hipLaunchKernelGGL(k_pack_weights_bf16, dim3((unsigned)((total + kWqThreads - 1) / kWqThreads)),
+                       dim3(kWqThreads), 0, as_stream(stream), w, Cin, kt, kh, kw, total, wp);
+    return launch_status();
+}
+
 extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, int kh, int kw,
                                      float clip_ratio, int8_t *wq, float *w_scale, void *stream)
 {
-    if (force_fail()) return QVAE_EFORCED;
+    if (force_fail(true)) return QVAE_EFORCED;
     if (!w || !wq || !w_scale || Cout <= 0 || Cin <= 0 || kt <= 0 || kh <= 0 || kw <= 0)
         return QVAE_EINVAL;
     if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN

@@ -14,6 +14,10 @@ Names follow the C entry points:
   act_absmax_quant        -> qvae_act_absmax_quant
   causalconv3d_w8a8       -> qvae_causalconv3d_w8a8
   causalconv3d_w8a8_acc32 -> qvae_causalconv3d_w8a8_acc32
+  causalconv3d_w8a8_absmax -> qvae_causalconv3d_w8a8_absmax
+  select_layer            -> qvae_select_layer
+  pack_weights_bf16       -> qvae_pack_weights_bf16
+  causalconv3d_bf16       -> qvae_causalconv3d_bf16
 """
 from __future__ import annotations
 
@@ -26,6 +30,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqvae.so")
 
 OK, EINVAL, EUNSUPPORTED, ELAUNCH, EFORCED = 0, -1, -2, -3, -4
+PRESET_NATIVE, PRESET_CONSERVATIVE, PRESET_BALANCED, PRESET_AGGRESSIVE = 0, 1, 2, 3
+PRESETS = {"native": PRESET_NATIVE, "conservative": PRESET_CONSERVATIVE, "balanced": PRESET_BALANCED,
+           "aggressive": PRESET_AGGRESSIVE}
 ABSMAX_WORDS = 513   # QVAE_ABSMAX_WORDS: word 0 = bf16 bits of max|x|, then partial maxima
 
 
@@ -66,6 +73,12 @@ def lib() -> ctypes.CDLL:
         L.qvae_causalconv3d_w8a8_absmax.restype = i32
         L.qvae_causalconv3d_w8a8_acc32.argtypes = [P, P, P] + [i32] * 9 + [P, P]
         L.qvae_causalconv3d_w8a8_acc32.restype = i32
+        L.qvae_select_layer.argtypes = [i32, ctypes.c_char_p] + [i32] * 6
+        L.qvae_select_layer.restype = i32
+        L.qvae_pack_weights_bf16.argtypes = [P] + [i32] * 5 + [P, P]
+        L.qvae_pack_weights_bf16.restype = i32
+        L.qvae_causalconv3d_bf16.argtypes = [P, P, P, P] + [i32] * 9 + [P, P]
+        L.qvae_causalconv3d_bf16.restype = i32
         _lib = L
     return _lib
 
@@ -116,6 +129,34 @@ def quantize_weights(w: torch.Tensor, clip_ratio: float = 1.0, stream=None):
     _check(lib().qvae_quantize_weights(_p(w), Cout, Cin, kt, kh, kw, float(clip_ratio),
                                        _p(wq), _p(ws), _stream(stream)), "qvae_quantize_weights")
     return wq, ws
+
+
+def packed_weight_shape_bf16(Cout, Cin, kt, kh, kw):
+    """Shape of the packed bf16 weights: [Cout/32][kt][Cin/16][kh][kw][64][8]."""
+    return (Cout // 32, kt, Cin // 16, kh, kw, 64, 8)
+
+
+def pack_weights_bf16(w: torch.Tensor, stream=None):
+    """w bf16 [Cout][Cin][kt][kh][kw] -> packed bf16 [Cout/32][kt][Cin/16][kh][kw][64][8]
+    (a permutation; see qvae.h)."""
+    _dev(w, "w", torch.bfloat16)
+    Cout, Cin, kt, kh, kw = w.shape
+    if Cout % 32 or Cin % 16:
+        raise QvaeError(EUNSUPPORTED, "pack_weights_bf16: Cout must be a multiple of 32, Cin of 16")
+    wp = torch.empty(packed_weight_shape_bf16(Cout, Cin, kt, kh, kw), dtype=torch.bfloat16, device=w.device)
+    _check(lib().qvae_pack_weights_bf16(_p(w), Cout, Cin, kt, kh, kw, _p(wp), _stream(stream)),
+           "qvae_pack_weights_bf16")
+    return wp
+
+
+def select_layer(preset, name: str, Cin: int, Cout: int, k=(3, 3, 3), top_channels: int = 384) -> bool:
+    """True if the preset runs this decoder Conv3d in W8A8 (host-side plan)."""
+    p = PRESETS[preset] if isinstance(preset, str) else int(preset)
+    r = lib().qvae_select_layer(p, name.encode(), int(Cin), int(Cout), int(k[0]), int(k[1]), int(k[2]),
+                                int(top_channels))
+    if r < 0:
+        raise QvaeError(r, "qvae_select_layer")
+    return r == 1
 
 
 # ------------------------------------------------------------------ activations
@@ -237,6 +278,35 @@ def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Ten
         out = torch.empty((N, T, H, W, Cout), dtype=torch.int32, device=xq.device)
     _check(lib().qvae_causalconv3d_w8a8_acc32(_p(xq), _p(cache), _p(wq), N, T, H, W, Cin, Cout, kt, kh, kw,
                                               _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_acc32")
+    return out
+
+
+def causalconv3d_bf16(x: torch.Tensor, wp: torch.Tensor, bias: torch.Tensor | None = None,
+                      cache: torch.Tensor | None = None, out: torch.Tensor | None = None, stream=None):
+    """Native-precision conv: x bf16 [N][T][H][W][Cin], wp from pack_weights_bf16,
+    cache bf16 [N][kt-1][H][W][Cin] or None -> y bf16 [N][T][H][W][Cout]."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(wp, "wp", torch.bfloat16)
+    N, T, H, W, Cin = x.shape
+    if wp.dim() != 7 or tuple(wp.shape[5:]) != (64, 8):
+        raise ValueError("wp must be the packed [Cout/32][kt][Cin/16][kh][kw][64][8] tensor")
+    Cout, kt, Cin2, kh, kw = wp.shape[0] * 32, wp.shape[1], wp.shape[2] * 16, wp.shape[3], wp.shape[4]
+    if Cin2 != Cin:
+        raise ValueError(f"Cin mismatch: x has {Cin}, wp has {Cin2}")
+    if cache is not None:
+        _dev(cache, "cache", torch.bfloat16)
+        if tuple(cache.shape) != (N, kt - 1, H, W, Cin):
+            raise ValueError(f"cache must be [N][kt-1][H][W][Cin] = {(N, kt - 1, H, W, Cin)}")
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+    if out is None:
+        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=x.device)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if tuple(out.shape) != (N, T, H, W, Cout):
+            raise ValueError("out shape")
+    _check(lib().qvae_causalconv3d_bf16(_p(x), _p(cache), _p(wp), _p(bias), N, T, H, W, Cin, Cout, kt, kh, kw,
+                                        _p(out), _stream(stream)), "qvae_causalconv3d_bf16")
     return out
 
 
