@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "INT8 TOPS & ms/layer of W8A8 CausalConv3d (% MFMA peak); quant-pass HBM GB/s"
 PEAK_INT8_TOPS = 5000.0       # MI355X dense INT8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E, 8 TB/s
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 
 
 def layer_counts(spec, cache: bool):
@@ -203,6 +204,96 @@ def operand_probe(args):
     print(json.dumps(out))
 
 
+def decoder_stack(args):
+    """The 28 residual-block convs of the decoder at one output size, run as
+    each preset says (W8A8 layer step = absmax + quantize + INT8 conv, native =
+    bf16 conv), timed as one stack per preset."""
+    import numpy as np
+    import torch
+
+    from w8a8_int8_quantized_act_amd import decoder, ops
+
+    dev = "cuda:0"
+    L = ops.lib()
+    P = ctypes.c_void_p
+    stream = torch.cuda.current_stream()
+    sp = P(stream.cuda_stream)
+    layers = decoder.residual_convs(args.out_h, args.out_w)
+    g = torch.Generator(device=dev).manual_seed(7)
+    data = []
+    for spec in layers:
+        w = (torch.randn(spec.Cout, spec.Cin, 3, 3, 3, generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        b = torch.randn(spec.Cout, generator=g, device=dev) * 0.01
+        x = torch.randn(1, 1, spec.H, spec.W, spec.Cin, generator=g, device=dev)
+        x = (x * torch.sigmoid(x)).to(torch.bfloat16)
+        wq, ws = ops.quantize_weights(w.float())
+        wp = ops.pack_weights_bf16(w)
+        d = dict(spec=spec, x=x, b=b, wq=wq, ws=ws, wp=wp,
+                 xq=torch.empty(x.shape, dtype=torch.int8, device=dev),
+                 xs=torch.empty((1,), dtype=torch.float32, device=dev),
+                 am=torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=dev),
+                 y=torch.empty((1, 1, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev))
+        dims = (1, 1, spec.H, spec.W, spec.Cin, spec.Cout, 3, 3, 3)
+        d["w8a8"] = [(L.qvae_act_absmax, (P(x.data_ptr()), x.numel(), P(d["am"].data_ptr()), sp)),
+                     (L.qvae_act_quantize, (P(x.data_ptr()), x.numel(), ctypes.c_float(1.0), P(d["am"].data_ptr()),
+                                            P(d["xs"].data_ptr()), P(d["xq"].data_ptr()), sp)),
+                     (L.qvae_causalconv3d_w8a8, (P(d["xq"].data_ptr()), P(d["xs"].data_ptr()), None,
+                                                 P(wq.data_ptr()), P(ws.data_ptr()), P(b.data_ptr()), *dims,
+                                                 P(d["y"].data_ptr()), sp))]
+        d["native"] = [(L.qvae_causalconv3d_bf16, (P(x.data_ptr()), None, P(wp.data_ptr()), P(b.data_ptr()), *dims,
+                                                   P(d["y"].data_ptr()), sp))]
+        d["ops"] = 2 * spec.Cout * spec.Cin * 9 * spec.H * spec.W      # T = 1: the two front frames are padding
+        data.append(d)
+
+    def timed(calls, k):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        rc = 0
+        for _ in range(k):
+            for f, a in calls:
+                rc |= f(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert rc == 0
+        return e0.elapsed_time(e1) / k
+
+    total_ops = sum(d["ops"] for d in data)
+    presets = {}
+    for preset in ("native", "conservative", "balanced", "aggressive"):
+        pl = decoder.plan(preset, layers)
+        calls = [c for d in data for c in (d["w8a8"] if pl[d["spec"].name] else d["native"])]
+        timed(calls, 2)
+        ms = float(np.median([timed(calls, args.steps) for _ in range(3)]))
+        presets[preset] = {"w8a8_layers": sum(pl.values()), "ms_per_stack": round(ms, 4),
+                           "TOPS": round(total_ops / (ms * 1e-3) / 1e12, 1)}
+    base = presets["native"]["ms_per_stack"]
+    for v in presets.values():
+        v["speedup_vs_native"] = round(base / v["ms_per_stack"], 3)
+    # each distinct layer shape alone: native bf16 conv and the W8A8 step / conv
+    shapes = {}
+    for d in data:
+        s = d["spec"]
+        key = f"{s.Cin}->{s.Cout} @{s.H}x{s.W}"
+        if key in shapes:
+            continue
+        nat = timed(d["native"], args.steps)
+        step = timed(d["w8a8"], args.steps)
+        conv = timed(d["w8a8"][2:], args.steps)
+        shapes[key] = {"alg_GOP": round(d["ops"] / 1e9, 2),
+                       "native_conv_ms": round(nat, 5),
+                       "native_TFLOPs": round(d["ops"] / (nat * 1e-3) / 1e12, 1),
+                       "native_frac_of_bf16_peak": round(d["ops"] / (nat * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "w8a8_step_ms": round(step, 5), "w8a8_conv_ms": round(conv, 5),
+                       "w8a8_conv_frac_of_int8_peak": round(d["ops"] / (conv * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)}
+    print(json.dumps({"probe": "decoder conv stack by preset", "output": f"{args.out_h}x{args.out_w}",
+                      "layers": len(layers), "alg_GOP_per_stack": round(total_ops / 1e9, 1),
+                      "steps": args.steps, "presets": presets, "per_shape": shapes,
+                      "note": "W8A8 layer = absmax + quantize + INT8 conv; native layer = bf16 conv (FP32 "
+                              "accumulation); each layer has its own resident input; HIP events around K "
+                              "back-to-back stacks, median of 3"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +313,10 @@ def main():
                     help="a multi-frame variant: the layer's shape with T frames (redrawn, same recipe)")
     ap.add_argument("--clip", type=float, default=1.0,
                     help="activation and weight clip ratio in (0, 1] (the page fixes 1.0)")
+    ap.add_argument("--decoder", action="store_true",
+                    help="only time the decoder's 28 residual-block convs per preset (W8A8 vs native bf16)")
+    ap.add_argument("--out-h", type=int, default=1024)
+    ap.add_argument("--out-w", type=int, default=1024)
     args = ap.parse_args()
 
     if args.copy_probe:
@@ -240,6 +335,9 @@ def main():
         return
     if args.first_calls:
         first_calls()
+        return
+    if args.decoder:
+        decoder_stack(args)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
