@@ -126,6 +126,42 @@ int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
                           void *stream);
 
 /*
+ * The norm + SiLU pass in front of a decoder residual conv, h = SiLU(RMSNorm(x))
+ * over the channels of every pixel (the absorption of a preceding RMSNorm by
+ * the activation quantizer: page "Doubling LLM token rates in ComfyUI"
+ * (ComfyUI v0.45.0), section "Optimizing linear kernels"; that the VAE's
+ * residual convs sit behind norm and SiLU is a reading).  Per pixel, in IEEE
+ * binary32, every step rounded as written:
+ *   ss = 0; ss = fma(x_c, x_c, ss) for c = 0, 1, ..., C-1 (in this order)
+ *   r  = 1 / sqrt(ss / C + eps)
+ *   n_c = (x_c * r) * gamma[c]
+ *   h_c = bf16_rne(n_c / (1 + E(-n_c)))
+ * where E(y) approximates exp(y) by Cody-Waite reduction and a Taylor
+ * polynomial (within a few binary32 ulps; the steps are in
+ * csrc/qvae_norm.hip and the oracle):  y' = clamp(y, -104, 89),
+ * k = rint(y' * fl(log2 e)), r' = fma(k, -0x1.62e4p-1, y'),
+ * r' = fma(k, -0x1.7f7d1cp-20, r'), p = Horner with fma of 1/i!, i = 6..0, at r',
+ * E = ldexp(p, k).
+ *   x      bf16 bit patterns [npix][C] (channels-last; npix = N*T*H*W)
+ *   gamma  float32 [C]
+ *   eps    > 0 (finite)
+ *   h      bf16 bit patterns [npix][C] out
+ * Supported: C % 8 == 0, 8 <= C <= 480.  eps <= 0, NaN or infinite: QVAE_EINVAL.
+ */
+int qvae_rmsnorm_silu(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps, uint16_t *h,
+                      void *stream);
+
+/*
+ * qvae_rmsnorm_silu that also leaves the partial maxima of |h| in an
+ * activation-maximum buffer (words 1..; word 0 untouched), exactly as
+ * qvae_act_absmax would for h: qvae_act_quantize(h, h_absmax, ...) then
+ * quantizes h for the W8A8 conv without an absmax pass.  A W8A8 call
+ * (QVAE_FORCE_FAIL=w8a8 fails it); h_absmax == NULL is QVAE_EINVAL.
+ */
+int qvae_rmsnorm_silu_absmax(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps,
+                             uint16_t *h, uint32_t *h_absmax, void *stream);
+
+/*
  * W8A8 causal 3-D convolution as an implicit GEMM (intro paragraph: the
  * implicit-GEMM kernel for CausalConv3d; scheme paragraph: INT8 x INT8 with
  * INT32 accumulation, FP32 rescale, output in the activation precision).

@@ -77,6 +77,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_layer.restype = i32
         L.oracle_conv_bf16_positions.argtypes = [P, P, P, P] + [i32] * 9 + [P, i64, P, P]
         L.oracle_conv_bf16_positions.restype = i32
+        L.oracle_exp_cw.argtypes = [f32]
+        L.oracle_exp_cw.restype = f32
+        L.oracle_silu_cw.argtypes = [f32]
+        L.oracle_silu_cw.restype = f32
+        L.oracle_rmsnorm_silu.argtypes = [P, i64, i32, P, f32, P]
+        L.oracle_rmsnorm_silu.restype = i32
         _lib = L
     return _lib
 
@@ -262,3 +268,27 @@ def conv_bf16(x_bf16_bits, w_bf16_bits, bias=None, cache=None, positions=None):
     if rc != OK:
         raise ValueError(f"oracle bf16 conv failed: {rc}")
     return z, mag
+
+
+# ---------------------------------------------------------------- RMSNorm + SiLU
+def exp_cw(y: float) -> np.float32:
+    """The binary32 exp of the norm + SiLU pass (Cody-Waite + Taylor)."""
+    return np.float32(lib().oracle_exp_cw(float(np.float32(y))))
+
+
+def silu_cw(n: float) -> np.float32:
+    return np.float32(lib().oracle_silu_cw(float(np.float32(n))))
+
+
+def rmsnorm_silu(x_bf16_bits: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """x uint16 bf16 bits [..., C] (channels last) -> h uint16 bf16 bits, same shape."""
+    x = _c(x_bf16_bits, np.uint16)
+    g = _c(gamma, np.float32)
+    C = x.shape[-1]
+    if g.shape != (C,):
+        raise ValueError("gamma must be [C]")
+    h = np.empty(x.shape, np.uint16)
+    rc = lib().oracle_rmsnorm_silu(_ptr(x), x.size // C, C, _ptr(g), float(np.float32(eps)), _ptr(h))
+    if rc != OK:
+        raise ValueError(f"oracle rmsnorm_silu failed: {rc}")
+    return h

@@ -350,6 +350,63 @@ int oracle_conv_bf16_positions(const uint16_t *x, const uint16_t *cache,
     return status;
 }
 
+/* ---- RMSNorm + SiLU in front of a residual conv ---------------------------
+ * The activation the quantizer sees in a decoder residual block is
+ * SiLU(RMSNorm(x)) (the absorption of a preceding RMSNorm by the activation
+ * quantizer: page "Doubling LLM token rates in ComfyUI" (ComfyUI v0.45.0),
+ * section "Optimizing linear kernels"; the norm-SiLU-conv order of the VAE's
+ * residual blocks is a reading).  Per pixel of C channels, every step one
+ * IEEE binary32 operation, in this order:
+ *   ss = 0; ss = fma(x_c, x_c, ss) for c = 0 .. C-1
+ *   r  = 1 / sqrt(ss / C + eps)
+ *   n  = (x_c * r) * gamma_c
+ *   h  = bf16_rne(n / (1 + E(-n)))
+ * E is exp by Cody-Waite range reduction and a Taylor polynomial: clamp the
+ * argument to [-104, 89], k = rint(y * log2 e), reduce with ln 2 split in a
+ * short high part (exact products with k) and the remainder, evaluate
+ * 1 + r + r^2/2! + ... + r^6/6! by Horner with fma, scale by 2^k. */
+static float exp_cody_waite(float y)
+{
+    const float log2e = 0x1.715476p+0f;      /* binary32 nearest log2(e)        */
+    const float ln2_hi = 0x1.62e4p-1f;       /* ln 2 to 8 significant bits      */
+    const float ln2_lo = 0x1.7f7d1cp-20f;    /* binary32 nearest ln 2 - ln2_hi  */
+    const float inv_fact[7] = {1.0f, 1.0f, 0.5f, 0x1.555556p-3f, 0x1.555556p-5f,
+                               0x1.111112p-7f, 0x1.6c16c2p-10f};   /* 1/i!, i = 0..6 */
+    if (y < -104.0f) y = -104.0f;
+    if (y > 89.0f) y = 89.0f;
+    float k = rintf(y * log2e);
+    float r = fmaf(k, -ln2_hi, y);
+    r = fmaf(k, -ln2_lo, r);
+    float p = inv_fact[6];
+    for (int i = 5; i >= 0; --i) p = fmaf(p, r, inv_fact[i]);
+    return ldexpf(p, (int)k);
+}
+
+float oracle_exp_cw(float y) { return exp_cody_waite(y); }
+
+float oracle_silu_cw(float n) { return n / (1.0f + exp_cody_waite(-n)); }
+
+int oracle_rmsnorm_silu(const uint16_t *x, int64_t npix, int C, const float *gamma,
+                        float eps, uint16_t *h)
+{
+    if (!x || !gamma || !h || npix <= 0 || C <= 0 || !(eps > 0.0f)) return ORACLE_EARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t p = 0; p < npix; ++p) {
+        const uint16_t *xp = x + p * C;
+        float ss = 0.0f;
+        for (int c = 0; c < C; ++c) {
+            float v = oracle_bf16_to_f32(xp[c]);
+            ss = fmaf(v, v, ss);
+        }
+        float r = 1.0f / sqrtf(ss / (float)C + eps);
+        for (int c = 0; c < C; ++c) {
+            float n = (oracle_bf16_to_f32(xp[c]) * r) * gamma[c];
+            h[p * C + c] = oracle_f32_to_bf16(oracle_silu_cw(n));
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* ---- the whole layer, end to end (used for CPU timing) -------------------
  * x bf16 [N][T][H][W][Cin] -> y bf16 [N][T][H][W][Cout] for the positions in
  * pos (all positions when pos is NULL and npos = N*T*H*W).  xq and acc are

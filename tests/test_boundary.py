@@ -35,6 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ["qvae_quantize_weights", "qvae_act_absmax", "qvae_act_quantize", "qvae_act_absmax_quant",
               "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_absmax", "qvae_causalconv3d_w8a8_acc32",
               "qvae_select_layer", "qvae_pack_weights_bf16", "qvae_causalconv3d_bf16",
+              "qvae_rmsnorm_silu", "qvae_rmsnorm_silu_absmax",
               "qvae_strerror", "qvae_version"]:
         assert n in names
 
@@ -135,6 +136,19 @@ def test_bf16_entry_points_reject(L):
     assert p(FAKE, 32, 0, 3, 3, 3, FAKE, None) == -1
     assert p(FAKE, 40, 32, 3, 3, 3, FAKE, None) == -2
     assert p(FAKE, 32, 24, 3, 3, 3, FAKE, None) == -2
+
+
+def test_rmsnorm_silu_rejects(L):
+    f, fa = L.qvae_rmsnorm_silu, L.qvae_rmsnorm_silu_absmax
+    assert f(None, 4, 96, FAKE, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 0, 96, FAKE, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 4, 96, None, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 4, 96, FAKE, 0.0, FAKE, None) == -1
+    assert f(FAKE, 4, 96, FAKE, float("nan"), FAKE, None) == -1
+    assert f(FAKE_MIS, 4, 96, FAKE, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 4, 100, FAKE, 1e-6, FAKE, None) == -2       # C % 8
+    assert f(FAKE, 4, 512, FAKE, 1e-6, FAKE, None) == -2       # C > 480
+    assert fa(FAKE, 4, 96, FAKE, 1e-6, FAKE, None, None) == -1  # no maximum buffer
 
 
 def test_force_fail_hook():

@@ -1,0 +1,110 @@
+"""GPU parity of the norm + SiLU pass (with and without the fused activation
+maximum) against the oracle, through the C ABI.  The pass and the oracle
+perform the same binary32 steps (the sequence is stated in qvae.h), so h is
+compared bit for bit, and so are the quantizer's scale and codes of h."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.layout import pack_weight_codes
+from tests.test_gpu_parity import DEV, bf16_bits, f32_bits, sample_positions, to_dev_bits, ulp_dist
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from w8a8_int8_quantized_act_amd import ops as o
+    o.lib()
+    return o
+
+
+def _draw(seed, npix, C, kind="silu", scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(npix, C, generator=g) * scale
+    if kind == "silu":
+        x = x * torch.sigmoid(x)
+    if npix > 5:
+        x[5] = 0.0                                         # an all-zero pixel
+    gamma = (1.0 + 0.2 * torch.randn(C, generator=g)).float()
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), gamma.numpy()
+
+
+CASES = [(1, 8, 1e-6), (7, 96, 1e-6), (1000, 96, 1e-6), (333, 192, 0.1), (129, 384, 1e-6), (16384, 384, 1e-6),
+         (4097, 480, 1e-6), (3001, 16, 1e-3), (65536 + 17, 192, 1e-6)]
+
+
+@pytest.mark.parametrize("npix,C,eps", CASES, ids=[f"{c[0]}x{c[1]}_eps{c[2]:g}" for c in CASES])
+def test_rmsnorm_silu_bitexact(ops, npix, C, eps):
+    xb, gamma = _draw(900 + C + npix % 97, npix, C)
+    x = to_dev_bits(xb).view(npix, C)
+    gd = torch.from_numpy(gamma).to(DEV)
+    h = ops.rmsnorm_silu(x, gd, eps)
+    stale = torch.full((ops.ABSMAX_WORDS,), 0x7F7F, dtype=torch.int32, device=DEV)
+    h2, am = ops.rmsnorm_silu(x, gd, eps, absmax_bits=stale, with_absmax=True)
+    xs, xq = ops.act_quantize(h2, am)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_silu(xb.reshape(npix, C), gamma, eps)
+    got = bf16_bits(h)
+    bad = np.count_nonzero(got != ref)
+    assert bad == 0, f"{bad} of {ref.size} values differ, first at {np.argwhere(got != ref)[:3].tolist()}"
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    a, s, q = oracle.act_absmax_quant(ref)
+    assert int(am[0].item()) == f32_bits(a) >> 16
+    assert f32_bits(xs.item()) == f32_bits(s)
+    assert np.array_equal(xq.cpu().numpy(), q)
+
+
+def test_rmsnorm_silu_full_level_and_large_values(ops):
+    # the 96-channel level at 1024 x 1024 (100 M values), and inputs scaled by 1000
+    for npix, C, scale, seed in [(1024 * 1024, 96, 1.0, 950), (50000, 96, 1000.0, 951)]:
+        xb, gamma = _draw(seed, npix, C, kind="normal", scale=scale)
+        x = to_dev_bits(xb).view(npix, C)
+        h, am = ops.rmsnorm_silu(x, torch.from_numpy(gamma).to(DEV), 1e-6, with_absmax=True)
+        xs, xq = ops.act_quantize(h, am)
+        torch.cuda.synchronize()
+        ref = oracle.rmsnorm_silu(xb.reshape(npix, C), gamma, 1e-6)
+        assert np.array_equal(bf16_bits(h), ref)
+        a, s, q = oracle.act_absmax_quant(ref)
+        assert f32_bits(xs.item()) == f32_bits(s)
+        assert np.array_equal(xq.cpu().numpy(), q)
+
+
+def test_residual_branch_norm_silu_quantize_conv(ops):
+    """x -> RMSNorm + SiLU (with the fused maximum) -> quantize (no absmax pass)
+    -> W8A8 conv, against the oracle's h, its quantizer and its conv."""
+    N, T, H, W, C = 1, 2, 37, 45, 192
+    xb, gamma = _draw(960, N * T * H * W, C, kind="normal")
+    g = torch.Generator().manual_seed(961)
+    w = (torch.randn(C, C, 3, 3, 3, generator=g) * 0.03).numpy()
+    b = (torch.randn(C, generator=g) * 0.01).numpy()
+    x = to_dev_bits(xb).view(N, T, H, W, C)
+    h, am = ops.rmsnorm_silu(x, torch.from_numpy(gamma).to(DEV), 1e-6, with_absmax=True)
+    xs, xq = ops.act_quantize(h, am)
+    wq_d, ws_d = ops.quantize_weights(torch.from_numpy(w).to(DEV))
+    y = ops.causalconv3d_w8a8(xq, xs, wq_d, ws_d, torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    href = oracle.rmsnorm_silu(xb.reshape(N, T, H, W, C), gamma, 1e-6)
+    wq, ws = oracle.quantize_weights(w)
+    pos = sample_positions(N, T, H, W, 400, 17)
+    yref, s = oracle.layer(href, wq, ws, b, positions=pos)
+    assert f32_bits(xs.item()) == f32_bits(s)
+    assert ulp_dist(bf16_bits(y.reshape(-1, C)[torch.from_numpy(pos).to(DEV)]), yref).max() == 0
+
+
+def test_rmsnorm_silu_rejects(ops):
+    x = torch.zeros(4, 96, dtype=torch.bfloat16, device=DEV)
+    gd = torch.ones(96, device=DEV)
+    for eps in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(ops.QvaeError) as e:
+            ops.rmsnorm_silu(x, gd, eps)
+        assert e.value.status == ops.EINVAL
+    with pytest.raises(ops.QvaeError) as e:
+        ops.rmsnorm_silu(torch.zeros(4, 100, dtype=torch.bfloat16, device=DEV), torch.ones(100, device=DEV))
+    assert e.value.status == ops.EUNSUPPORTED
+    with pytest.raises(ops.QvaeError) as e:
+        ops.rmsnorm_silu(torch.zeros(4, 512, dtype=torch.bfloat16, device=DEV), torch.ones(512, device=DEV))
+    assert e.value.status == ops.EUNSUPPORTED

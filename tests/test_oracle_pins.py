@@ -563,3 +563,82 @@ def test_bf16_conv_zero_cache_and_causality(oracle):
     pos = np.array([0, 7, 29, N * T * H * W - 1])
     zp, _ = oracle.conv_bf16(x, w, positions=pos)
     assert np.array_equal(zp, z0.reshape(-1, Cout)[pos])
+
+
+# --------------------------------------------------------------- RMSNorm + SiLU prologue
+def test_exp_cw_against_libm(oracle):
+    import math
+    ys = np.linspace(-87.0, 88.0, 20001).astype(np.float32)
+    worst = 0.0
+    for y in ys[::3]:
+        e = float(oracle.exp_cw(y))
+        ref = math.exp(float(y))
+        worst = max(worst, abs(e - ref) / ref)
+    assert worst <= 4 * 2.0 ** -24, worst
+    assert oracle.exp_cw(0.0) == 1.0
+    for k in range(-20, 21):                              # y = k ln2 (rounded) -> about 2^k
+        y = np.float32(k * math.log(2))
+        assert abs(float(oracle.exp_cw(y)) / math.exp(float(y)) - 1) <= 4 * 2.0 ** -24
+    assert oracle.exp_cw(-200.0) == 0.0                   # clamped: far below the smallest subnormal
+    assert np.isinf(oracle.exp_cw(200.0))                 # clamped at 89: overflows to +inf
+
+
+def test_silu_cw_against_float64(oracle):
+    import math
+    ns = np.concatenate([np.linspace(-30, 30, 6001), np.linspace(-1e-3, 1e-3, 201)]).astype(np.float32)
+    for n in ns[::2]:
+        ref = float(n) / (1.0 + math.exp(-float(n)))
+        got = float(oracle.silu_cw(n))
+        assert abs(got - ref) <= 8 * 2.0 ** -24 * abs(ref) + 1e-45, (n, got, ref)
+    assert oracle.silu_cw(0.0) == 0.0
+    assert float(oracle.silu_cw(-200.0)) == 0.0            # n / inf: -0
+    assert oracle.silu_cw(200.0) == np.float32(200.0)     # 1 + exp(-200) rounds to 1
+
+
+def _rmsnorm_silu_f64(xb, gamma, eps):
+    x = f32(xb).astype(np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    n = x * r * gamma.astype(np.float64)
+    return n / (1.0 + np.exp(-n))
+
+
+@pytest.mark.parametrize("C,eps,kind", [(96, 1e-6, "normal"), (384, 1e-6, "silu"), (192, 0.1, "normal"),
+                                        (8, 1e-6, "large")])
+def test_rmsnorm_silu_against_float64(oracle, C, eps, kind):
+    g = torch.Generator().manual_seed(40 + C)
+    x = torch.randn(500, C, generator=g)
+    if kind == "silu":
+        x = x * torch.sigmoid(x)
+    elif kind == "large":
+        x = x * 1000.0
+    x[3] = 0.0                                              # an all-zero pixel: h = 0
+    xb = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    gamma = (1.0 + 0.2 * torch.randn(C, generator=g)).numpy().astype(np.float32)
+    h = oracle.rmsnorm_silu(xb, gamma, eps)
+    ref = _rmsnorm_silu_f64(xb, gamma, eps)
+    hv = f32(h).astype(np.float64)
+    # bf16 rounding (half an ulp, <= 2^-8 relative) of a binary32 value within ~16 ulps of the exact one
+    bound = 2.0 ** -8 * np.abs(ref) + 16 * 2.0 ** -24 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(hv - ref) <= bound)
+    refb = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(refb == h) >= 0.999
+    assert not h[3].any()
+    # gamma is per channel: swapping two channels' gammas swaps exactly those outputs' roles
+    g2 = gamma.copy()
+    g2[[0, 1]] = g2[[1, 0]]
+    h2 = oracle.rmsnorm_silu(xb, g2, eps)
+    assert np.array_equal(h2[:, 2:], h[:, 2:])
+
+
+def test_rmsnorm_silu_closed_form(oracle):
+    # a pixel of equal powers of two: ss = C a^2 exactly, r = 1 / |a|, n = sign(a) * gamma
+    import math
+    C = 64
+    for a, gam in [(0.25, 2.0), (-4.0, 0.5), (1.0, 1.0)]:
+        xb = bits(np.full((1, C), a, np.float32))
+        h = oracle.rmsnorm_silu(xb, np.full(C, gam, np.float32), 2.0 ** -40)
+        n = math.copysign(gam, a)
+        ref = n / (1 + math.exp(-n))
+        expect = np.float32(ref).view(np.uint32)
+        expect = (expect + 0x7FFF + ((expect >> 16) & 1)) >> 16        # bf16 round-to-nearest-even
+        assert np.all(h == expect), (a, gam, h[0, 0], expect)

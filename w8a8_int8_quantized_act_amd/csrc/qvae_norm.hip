@@ -1,0 +1,233 @@
+// qvae_norm.hip -- the norm + SiLU pass in front of a decoder residual conv,
+// with the activation maximum of its output fused in (gfx950).
+//
+// Why it is here: the W8A8 activation quantizer needs the maximum of the
+// conv's input before it can emit a single code (page "ComfyUI-Qwen-VAE-Triton
+// v0.2.0", section "Three presets explained": dynamic symmetric INT8
+// activations).  In the decoder that input is SiLU(RMSNorm(x)), produced by a
+// pass that reads x and writes the bf16 result anyway; letting that pass also
+// leave the partial maxima of its output removes the quantizer's own absmax
+// pass (a read of the whole tensor).  The absorption of the preceding RMSNorm
+// by the activation quantizer is the prologue fusion of ComfyUI's INT8
+// linear kernels (page "Doubling LLM token rates in ComfyUI" (ComfyUI
+// v0.45.0), section "Optimizing linear kernels"); that the VAE's residual
+// convs sit behind norm and SiLU is a reading of the residual-block layer
+// names the presets use.
+//
+// What it computes, per pixel (C channels, channels-last), in IEEE binary32
+// with every step rounded as written (the oracle performs the same steps):
+//   ss  = 0;  ss = fma(x_c, x_c, ss) for c = 0, 1, ..., C-1 (in this order)
+//   r   = 1 / sqrt(ss / C + eps)
+//   n_c = (x_c * r) * gamma_c
+//   h_c = bf16_rne(n_c / (1 + E(-n_c)))
+// with E(y) ~ exp(y) by Cody-Waite range reduction and a Taylor polynomial:
+//   y' = min(max(y, -104), 89);  k = rint(y' * log2(e));
+//   r' = fma(k, -ln2_hi, y');  r' = fma(k, -ln2_lo, r');
+//   p = Horner(1, 1, 1/2!, ..., 1/6!) at r' (fma at each step);  E = ldexp(p, k)
+// (|r'| <= ln2/2 + tiny; the truncation error r'^7/7! is below 2^-27 and E is
+// within a few units in the last place of exp).
+//
+// Layout of one pass.  A workgroup is 4 independent waves; a wave takes
+// chunks of P consecutive pixels (P*C*2 contiguous bytes), stages them in its
+// own LDS slice (coalesced 16-byte loads; pixel rows padded to 2C+16 bytes so
+// the row-per-lane reads below are conflict-free), lets lane p sum pixel p's
+// squares in channel order and leave its r, then processes the chunk's
+// 16-byte groups in memory order: 8 values of one pixel per lane, one 16-byte
+// store of bf16 results, a packed 16-bit running maximum of |h|.  Every
+// workgroup writes one partial maximum (the quantize pass reduces them).
+#include "qvae_internal.h"
+
+namespace qvae {
+
+typedef int v4i_n __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_n __attribute__((ext_vector_type(4)));
+typedef float f2_n __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2_n __attribute__((ext_vector_type(2)));
+
+constexpr int kNormThreads = 256;
+constexpr int kNormWaves = kNormThreads / 64;
+
+// exp(y) by the steps in the header (all binary32)
+__device__ __forceinline__ float exp_cw(float y)
+{
+    constexpr float kLog2e = 0x1.715476p+0f;
+    constexpr float kLn2Hi = 0x1.62e4p-1f;         // 8 significant bits: k * kLn2Hi is exact
+    constexpr float kLn2Lo = 0x1.7f7d1cp-20f;      // ln 2 - kLn2Hi
+    y = fminf(fmaxf(y, -104.0f), 89.0f);
+    const float k = __builtin_rintf(y * kLog2e);
+    float r = __builtin_fmaf(k, -kLn2Hi, y);
+    r = __builtin_fmaf(k, -kLn2Lo, r);
+    float p = 0x1.6c16c2p-10f;                     // 1/6!
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);      // 1/5!
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);      // 1/4!
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);      // 1/3!
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_amdgcn_ldexpf(p, (int)k);
+}
+
+__device__ __forceinline__ float silu_cw(float n) { return n / (1.0f + exp_cw(-n)); }
+
+// LDS written by some lanes of a wave and read by others of the same wave
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+template <int P, bool OUTMAX>
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm_silu(const uint16_t *__restrict__ x, int64_t npix, int C,
+                                                               const float *__restrict__ gamma, float eps,
+                                                               uint16_t *__restrict__ h, uint32_t *__restrict__ partials)
+{
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pitch = 2 * C + 16;
+    const int G = C >> 3;                                    // 16-byte groups per pixel
+    const int gamma_bytes = (C * 4 + 15) & ~15;
+    float *s_gamma = reinterpret_cast<float *>(smem);
+    char *s_x = smem + gamma_bytes + wave * (P * pitch + P * 4);
+    float *s_r = reinterpret_cast<float *>(s_x + P * pitch);
+    for (int c = tid; c < C; c += kNormThreads) s_gamma[c] = gamma[c];
+    __syncthreads();
+
+    const int64_t nchunks = (npix + P - 1) / P;
+    const float fC = (float)C;
+    uint32_t ymax = 0;
+    for (int64_t ch = (int64_t)blockIdx.x * kNormWaves + wave; ch < nchunks; ch += (int64_t)gridDim.x * kNormWaves) {
+        const int64_t p0 = ch * P;
+        const int np = (int)(npix - p0 < P ? npix - p0 : P);
+        const int bytes = np * C * 2;
+        const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x) + p0 * C, 0, bytes, 0x00020000);
+        // stage the chunk (16-byte loads in memory order)
+        for (int u = lane; u < P * G; u += 64) {
+            const int p = u / G, g = u - p * G;
+            const v4i_n v = __builtin_bit_cast(v4i_n, __builtin_amdgcn_raw_buffer_load_b128(rin, u * 16, 0, 0));
+            *reinterpret_cast<v4i_n *>(s_x + p * pitch + g * 16) = v;
+        }
+        wave_lds_sync();
+        // one lane per pixel: the sum of squares in channel order
+        if (lane < P) {
+            const char *row = s_x + lane * pitch;
+            float ss = 0.0f;
+            for (int g = 0; g < G; ++g) {
+                const v4i_n v = *reinterpret_cast<const v4i_n *>(row + g * 16);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t w = (uint32_t)v[k >> 1];
+                    const float xv = __uint_as_float((k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+                    ss = __builtin_fmaf(xv, xv, ss);
+                }
+            }
+            const float d = __builtin_sqrtf(ss / fC + eps);
+            s_r[lane] = 1.0f / d;
+        }
+        wave_lds_sync();
+        const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(h + p0 * C, 0, bytes, 0x00020000);
+        for (int u = lane; u < np * G; u += 64) {
+            const int p = u / G, g = u - p * G;
+            const v4i_n v = *reinterpret_cast<const v4i_n *>(s_x + p * pitch + g * 16);
+            const float r = s_r[p];
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t w = (uint32_t)v[k];
+                const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
+                const float n0 = (x0 * r) * s_gamma[g * 8 + 2 * k];
+                const float n1 = (x1 * r) * s_gamma[g * 8 + 2 * k + 1];
+                o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_n{silu_cw(n0), silu_cw(n1)}, bf2_n));
+                if constexpr (OUTMAX) ymax = pk_absmax(ymax, o[k]);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4_n{o[0], o[1], o[2], o[3]}, rout, u * 16, 0, 0);
+        }
+        wave_lds_sync();   // the next chunk overwrites this wave's slice
+    }
+
+    if constexpr (OUTMAX) {
+        __shared__ uint32_t s_red[kNormWaves];
+        const uint32_t m = wave_max_u32(max(ymax & 0xFFFFu, ymax >> 16));
+        if (lane == 0) s_red[wave] = m;
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t b = s_red[0];
+            for (int k = 1; k < kNormWaves; ++k) b = max(b, s_red[k]);
+            partials[blockIdx.x] = b;
+        }
+        if (blockIdx.x == 0)
+            for (int k = gridDim.x + tid; k < kAbsmaxParts; k += kNormThreads) partials[k] = 0;
+    }
+}
+
+// pixels per wave chunk for a channel count: the workgroup's LDS (gamma + 4
+// slices of P rows of 2C+16 bytes + P factors) stays within 64 KB
+static int norm_chunk_pixels(int C)
+{
+    auto lds = [C](int P) { return ((C * 4 + 15) & ~15) + kNormWaves * (P * (2 * C + 16) + P * 4); };
+    for (int P : {64, 32, 16})
+        if (lds(P) <= 65536) return P;
+    return 0;
+}
+
+static int norm_launch(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps, uint16_t *h,
+                       uint32_t *partials, hipStream_t st)
+{
+    const int P = norm_chunk_pixels(C);
+    if (P == 0) return QVAE_EUNSUPPORTED;
+    const size_t lds = ((C * 4 + 15) & ~15) + kNormWaves * ((size_t)P * (2 * C + 16) + P * 4);
+    const int64_t nchunks = (npix + P - 1) / P;
+    int64_t want = (nchunks + kNormWaves - 1) / kNormWaves;
+    const int64_t cap = partials ? kAbsmaxParts : (int64_t)device_cus() * 8;
+    const int grid = (int)(want < 1 ? 1 : (want > cap ? cap : want));
+#define QVAE_NORM_LAUNCH(PP)                                                                              \
+    if (partials)                                                                                         \
+        hipLaunchKernelGGL((k_rmsnorm_silu<PP, true>), dim3(grid), dim3(kNormThreads), lds, st, x, npix, C, \
+                           gamma, eps, h, partials);                                                      \
+    else                                                                                                  \
+        hipLaunchKernelGGL((k_rmsnorm_silu<PP, false>), dim3(grid), dim3(kNormThreads), lds, st, x, npix, C, \
+                           gamma, eps, h, partials);
+    if (P == 64) {
+        QVAE_NORM_LAUNCH(64)
+    } else if (P == 32) {
+        QVAE_NORM_LAUNCH(32)
+    } else {
+        QVAE_NORM_LAUNCH(16)
+    }
+#undef QVAE_NORM_LAUNCH
+    return launch_status();
+}
+
+static int norm_validate(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps, const uint16_t *h)
+{
+    if (!x || !gamma || !h || npix <= 0 || C <= 0) return QVAE_EINVAL;
+    if (!(eps > 0.0f) || eps > 3.0e38f) return QVAE_EINVAL;   // zero, negative, NaN or infinite
+    if (!aligned16(x) || !aligned16(h)) return QVAE_EINVAL;
+    if (C % 8 != 0 || norm_chunk_pixels(C) == 0) return QVAE_EUNSUPPORTED;
+    return QVAE_OK;
+}
+
+}  // namespace qvae
+
+using namespace qvae;
+
+extern "C" int qvae_rmsnorm_silu(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps,
+                                 uint16_t *h, void *stream)
+{
+    if (force_fail(false)) return QVAE_EFORCED;
+    const int rc = norm_validate(x, npix, C, gamma, eps, h);
+    if (rc != QVAE_OK) return rc;
+    return norm_launch(x, npix, C, gamma, eps, h, nullptr, as_stream(stream));
+}
+
+extern "C" int qvae_rmsnorm_silu_absmax(const uint16_t *x, int64_t npix, int C, const float *gamma, float eps,
+                                        uint16_t *h, uint32_t *h_absmax, void *stream)
+{
+    if (force_fail(true)) return QVAE_EFORCED;
+    if (!h_absmax) return QVAE_EINVAL;
+    const int rc = norm_validate(x, npix, C, gamma, eps, h);
+    if (rc != QVAE_OK) return rc;
+    return norm_launch(x, npix, C, gamma, eps, h, h_absmax + 1, as_stream(stream));
+}

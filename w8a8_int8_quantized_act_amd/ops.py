@@ -18,6 +18,8 @@ Names follow the C entry points:
   select_layer            -> qvae_select_layer
   pack_weights_bf16       -> qvae_pack_weights_bf16
   causalconv3d_bf16       -> qvae_causalconv3d_bf16
+  rmsnorm_silu            -> qvae_rmsnorm_silu
+  rmsnorm_silu_absmax     -> qvae_rmsnorm_silu_absmax
 """
 from __future__ import annotations
 
@@ -79,6 +81,10 @@ def lib() -> ctypes.CDLL:
         L.qvae_pack_weights_bf16.restype = i32
         L.qvae_causalconv3d_bf16.argtypes = [P, P, P, P] + [i32] * 9 + [P, P]
         L.qvae_causalconv3d_bf16.restype = i32
+        L.qvae_rmsnorm_silu.argtypes = [P, i64, i32, P, f32, P, P]
+        L.qvae_rmsnorm_silu.restype = i32
+        L.qvae_rmsnorm_silu_absmax.argtypes = [P, i64, i32, P, f32, P, P, P]
+        L.qvae_rmsnorm_silu_absmax.restype = i32
         _lib = L
     return _lib
 
@@ -204,6 +210,36 @@ def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None,
     _check(lib().qvae_act_absmax_quant(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                        _p(xq), _stream(stream)), "qvae_act_absmax_quant")
     return absmax_bits, x_scale, xq
+
+
+# ------------------------------------------------------------------ norm + SiLU prologue
+def rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, out: torch.Tensor | None = None,
+                 absmax_bits: torch.Tensor | None = None, with_absmax: bool = False, stream=None):
+    """h = SiLU(RMSNorm(x)) over the last (channel) axis of a channels-last bf16 tensor.
+
+    Returns h, or (h, absmax_bits) with ``with_absmax`` (the partial maxima of
+    |h| for act_quantize(h, absmax_bits))."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(gamma, "gamma", torch.float32)
+    C = x.shape[-1]
+    if gamma.shape != (C,):
+        raise ValueError("gamma must be [C]")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _dev(out, "out", torch.bfloat16)
+        if out.shape != x.shape:
+            raise ValueError("out shape")
+    npix = x.numel() // C
+    if with_absmax:
+        if absmax_bits is None:
+            absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=x.device)
+        _check(lib().qvae_rmsnorm_silu_absmax(_p(x), npix, C, _p(gamma), float(eps), _p(out), _p(absmax_bits),
+                                              _stream(stream)), "qvae_rmsnorm_silu_absmax")
+        return out, absmax_bits
+    _check(lib().qvae_rmsnorm_silu(_p(x), npix, C, _p(gamma), float(eps), _p(out), _stream(stream)),
+           "qvae_rmsnorm_silu")
+    return out
 
 
 # ------------------------------------------------------------------ convolution
