@@ -228,7 +228,9 @@ def decoder_stack(args):
         x = (x * torch.sigmoid(x)).to(torch.bfloat16)
         wq, ws = ops.quantize_weights(w.float())
         wp = ops.pack_weights_bf16(w)
-        d = dict(spec=spec, x=x, b=b, wq=wq, ws=ws, wp=wp,
+        gam = (1.0 + 0.1 * torch.randn(spec.Cin, generator=g, device=dev)).float()
+        d = dict(spec=spec, x=x, b=b, wq=wq, ws=ws, wp=wp, gam=gam,
+                 hb=torch.empty(x.shape, dtype=torch.bfloat16, device=dev),
                  xq=torch.empty(x.shape, dtype=torch.int8, device=dev),
                  xs=torch.empty((1,), dtype=torch.float32, device=dev),
                  am=torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=dev),
@@ -242,6 +244,22 @@ def decoder_stack(args):
                                                  P(d["y"].data_ptr()), sp))]
         d["native"] = [(L.qvae_causalconv3d_bf16, (P(x.data_ptr()), None, P(wp.data_ptr()), P(b.data_ptr()), *dims,
                                                    P(d["y"].data_ptr()), sp))]
+        # the residual branch: RMSNorm + SiLU of x into h, then the conv on h
+        npix, hp = spec.H * spec.W, P(d["hb"].data_ptr())
+        eps = ctypes.c_float(1e-6)
+        d["br_native"] = [(L.qvae_rmsnorm_silu, (P(x.data_ptr()), npix, spec.Cin, P(gam.data_ptr()), eps, hp, sp)),
+                          (L.qvae_causalconv3d_bf16, (hp, None, P(wp.data_ptr()), P(b.data_ptr()), *dims,
+                                                      P(d["y"].data_ptr()), sp))]
+        d["br_w8a8"] = [(L.qvae_rmsnorm_silu_absmax, (P(x.data_ptr()), npix, spec.Cin, P(gam.data_ptr()), eps, hp,
+                                                      P(d["am"].data_ptr()), sp)),
+                        (L.qvae_act_quantize, (hp, x.numel(), ctypes.c_float(1.0), P(d["am"].data_ptr()),
+                                               P(d["xs"].data_ptr()), P(d["xq"].data_ptr()), sp)),
+                        (L.qvae_causalconv3d_w8a8, (P(d["xq"].data_ptr()), P(d["xs"].data_ptr()), None,
+                                                    P(wq.data_ptr()), P(ws.data_ptr()), P(b.data_ptr()), *dims,
+                                                    P(d["y"].data_ptr()), sp))]
+        # the same branch without the fused maximum: norm + SiLU, then both quantizer passes
+        d["br_w8a8_unfused"] = [d["br_native"][0]] + [
+            (f, (hp,) + a[1:]) for f, a in d["w8a8"][:2]] + d["br_w8a8"][2:]
         d["ops"] = 2 * spec.Cout * spec.Cin * 9 * spec.H * spec.W      # T = 1: the two front frames are padding
         data.append(d)
 
@@ -270,6 +288,19 @@ def decoder_stack(args):
     base = presets["native"]["ms_per_stack"]
     for v in presets.values():
         v["speedup_vs_native"] = round(base / v["ms_per_stack"], 3)
+    # whole residual branches (norm + SiLU + conv) per preset; W8A8 layers with
+    # the maximum fused into the norm pass, and (for Aggressive) without it
+    branches = {}
+    for preset, key in (("native", "br_w8a8"), ("conservative", "br_w8a8"), ("balanced", "br_w8a8"),
+                        ("aggressive", "br_w8a8"), ("aggressive_unfused_absmax", "br_w8a8_unfused")):
+        pl = decoder.plan(preset.split("_")[0], layers)
+        calls = [c for d in data for c in (d[key] if pl[d["spec"].name] else d["br_native"])]
+        timed(calls, 2)
+        ms = float(np.median([timed(calls, args.steps) for _ in range(3)]))
+        branches[preset] = {"w8a8_layers": sum(pl.values()), "ms_per_stack": round(ms, 4)}
+    base_b = branches["native"]["ms_per_stack"]
+    for v in branches.values():
+        v["speedup_vs_native"] = round(base_b / v["ms_per_stack"], 3)
     # each distinct layer shape alone: native bf16 conv and the W8A8 step / conv
     shapes = {}
     for d in data:
@@ -280,18 +311,27 @@ def decoder_stack(args):
         nat = timed(d["native"], args.steps)
         step = timed(d["w8a8"], args.steps)
         conv = timed(d["w8a8"][2:], args.steps)
+        norm = timed(d["br_native"][:1], args.steps)
+        norm_mx = timed(d["br_w8a8"][:1], args.steps)
+        quant = timed(d["br_w8a8"][1:2], args.steps)
+        nbytes = 4 * s.H * s.W * s.Cin
         shapes[key] = {"alg_GOP": round(d["ops"] / 1e9, 2),
                        "native_conv_ms": round(nat, 5),
                        "native_TFLOPs": round(d["ops"] / (nat * 1e-3) / 1e12, 1),
                        "native_frac_of_bf16_peak": round(d["ops"] / (nat * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                        "w8a8_step_ms": round(step, 5), "w8a8_conv_ms": round(conv, 5),
-                       "w8a8_conv_frac_of_int8_peak": round(d["ops"] / (conv * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4)}
+                       "w8a8_conv_frac_of_int8_peak": round(d["ops"] / (conv * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                       "norm_silu_ms": round(norm, 5), "norm_silu_GBs": round(nbytes / (norm * 1e-3) / 1e9, 1),
+                       "norm_silu_absmax_ms": round(norm_mx, 5), "quantize_ms": round(quant, 5),
+                       "branch_native_ms": round(norm + nat, 5), "branch_w8a8_ms": round(norm_mx + quant + conv, 5)}
     print(json.dumps({"probe": "decoder conv stack by preset", "output": f"{args.out_h}x{args.out_w}",
                       "layers": len(layers), "alg_GOP_per_stack": round(total_ops / 1e9, 1),
-                      "steps": args.steps, "presets": presets, "per_shape": shapes,
-                      "note": "W8A8 layer = absmax + quantize + INT8 conv; native layer = bf16 conv (FP32 "
-                              "accumulation); each layer has its own resident input; HIP events around K "
-                              "back-to-back stacks, median of 3"}))
+                      "steps": args.steps, "presets": presets, "residual_branches": branches, "per_shape": shapes,
+                      "note": "presets: W8A8 layer = absmax + quantize + INT8 conv, native layer = bf16 conv "
+                              "(FP32 accumulation); residual_branches: each conv preceded by its RMSNorm + SiLU "
+                              "pass (native: norm + SiLU -> bf16 conv; W8A8: norm + SiLU with the fused maximum -> "
+                              "quantize -> INT8 conv); each layer has its own resident input; HIP events around "
+                              "K back-to-back stacks, median of 3"}))
 
 
 def main():

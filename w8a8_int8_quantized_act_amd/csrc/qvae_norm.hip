@@ -29,8 +29,9 @@
 //
 // Layout of one pass.  A workgroup is 4 independent waves; a wave takes
 // chunks of P consecutive pixels (P*C*2 contiguous bytes), stages them in its
-// own LDS slice (coalesced 16-byte loads; pixel rows padded to 2C+16 bytes so
-// the row-per-lane reads below are conflict-free), lets lane p sum pixel p's
+// own LDS slice (coalesced 16-byte loads, issued one chunk ahead into
+// registers; pixel rows padded to 2C+16 bytes so the row-per-lane reads below
+// are conflict-free), lets lane p sum pixel p's
 // squares in channel order and leave its r, then processes the chunk's
 // 16-byte groups in memory order: 8 values of one pixel per lane, one 16-byte
 // store of bf16 results, a packed 16-bit running maximum of |h|.  Every
@@ -46,6 +47,7 @@ typedef __bf16 bf2_n __attribute__((ext_vector_type(2)));
 
 constexpr int kNormThreads = 256;
 constexpr int kNormWaves = kNormThreads / 64;
+constexpr int kNormMaxLoads = 16;   // 16-byte loads per lane per chunk: P * C / 8 <= 1024 (see norm_chunk_pixels)
 
 // exp(y) by the steps in the header (all binary32)
 __device__ __forceinline__ float exp_cw(float y)
@@ -95,21 +97,40 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm_silu(const uint16_t *_
     __syncthreads();
 
     const int64_t nchunks = (npix + P - 1) / P;
+    const int64_t cstride = (int64_t)gridDim.x * kNormWaves;
     const float fC = (float)C;
+    const int nld = (P * G + 63) / 64;                       // 16-byte loads per lane per chunk
     uint32_t ymax = 0;
-    for (int64_t ch = (int64_t)blockIdx.x * kNormWaves + wave; ch < nchunks; ch += (int64_t)gridDim.x * kNormWaves) {
+    // The next chunk of this wave is loaded into registers while the current
+    // one is processed (its loads are waited for only when it is staged).
+    v4i_n pf[kNormMaxLoads];
+    auto load_chunk = [&](int64_t c) {
+        const int64_t q0 = c * P;
+        const int nq = (int)(npix - q0 < P ? npix - q0 : P);
+        const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(x) + q0 * C, 0, nq * C * 2, 0x00020000);   // pixels past the end read 0
+#pragma unroll
+        for (int k = 0; k < kNormMaxLoads; ++k)
+            if (k < nld)
+                pf[k] = __builtin_bit_cast(v4i_n, __builtin_amdgcn_raw_buffer_load_b128(rin, (lane + 64 * k) * 16, 0, 0));
+    };
+    int64_t ch = (int64_t)blockIdx.x * kNormWaves + wave;
+    if (ch < nchunks) load_chunk(ch);
+    for (; ch < nchunks; ch += cstride) {
         const int64_t p0 = ch * P;
         const int np = (int)(npix - p0 < P ? npix - p0 : P);
         const int bytes = np * C * 2;
-        const __amdgpu_buffer_rsrc_t rin = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t *>(x) + p0 * C, 0, bytes, 0x00020000);
-        // stage the chunk (16-byte loads in memory order)
-        for (int u = lane; u < P * G; u += 64) {
-            const int p = u / G, g = u - p * G;
-            const v4i_n v = __builtin_bit_cast(v4i_n, __builtin_amdgcn_raw_buffer_load_b128(rin, u * 16, 0, 0));
-            *reinterpret_cast<v4i_n *>(s_x + p * pitch + g * 16) = v;
+        // stage the chunk (16-byte pieces in memory order), then start the next one's loads
+#pragma unroll
+        for (int k = 0; k < kNormMaxLoads; ++k) {
+            const int u = lane + 64 * k;
+            if (k < nld && u < P * G) {
+                const int p = u / G, g = u - p * G;
+                *reinterpret_cast<v4i_n *>(s_x + p * pitch + g * 16) = pf[k];
+            }
         }
         wave_lds_sync();
+        if (ch + cstride < nchunks) load_chunk(ch + cstride);
         // one lane per pixel: the sum of squares in channel order
         if (lane < P) {
             const char *row = s_x + lane * pitch;
@@ -168,7 +189,7 @@ static int norm_chunk_pixels(int C)
 {
     auto lds = [C](int P) { return ((C * 4 + 15) & ~15) + kNormWaves * (P * (2 * C + 16) + P * 4); };
     for (int P : {64, 32, 16})
-        if (lds(P) <= 65536) return P;
+        if (lds(P) <= 65536 && P * (C / 8) <= 64 * kNormMaxLoads) return P;
     return 0;
 }
 
