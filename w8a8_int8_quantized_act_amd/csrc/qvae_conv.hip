@@ -96,6 +96,11 @@ struct ConvArgs {
     int tiles_w, tiles_h;
 };
 
+// Cache policy of the output stores: non-temporal (the output is not read
+// again by this kernel; measured 1-8 % faster than the default policy, most on
+// the store-heavy 96-channel layers, outputs identical).
+constexpr int kStoreNT = 2;
+
 // Halo pixels are stored with a 48-byte pitch (32 data bytes + 16 unused):
 // 3 is odd, so 16 consecutive pixels read by 16 consecutive lanes hit 16
 // distinct 16-byte bank groups.
@@ -615,7 +620,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                 const int pr = p / TW, pc = p - pr * TW;
                 const bool inside = tl.h0 + pr < H && tl.w0 + pc < W;
                 const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, kStoreNT);
             }
         };
         auto finish_all = [&](auto wkc) { static_for<HB>([&](auto jc) { finish_block(wkc, jc); }); };
