@@ -161,6 +161,14 @@ __device__ __forceinline__ uint2 quant8(u32x4 v, float s, float r, bool exact_on
     return o;
 }
 
+// 8 codes, non-temporal (nothing here reads them again; measured 2-10 % faster
+// for the pass than the default cache policy)
+__device__ __forceinline__ void store_codes(uint2 *dst, uint2 v)
+{
+    typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t *>(dst));
+}
+
 constexpr int kQuantThreads = 256;
 constexpr int kQuantUnroll = 4;   // 16-byte loads in flight per lane
 
@@ -202,9 +210,9 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
 #pragma unroll
             for (int u = 0; u < kQuantUnroll; ++u) v[u] = __builtin_nontemporal_load(&x16[i + u * stride]);
 #pragma unroll
-            for (int u = 0; u < kQuantUnroll; ++u) q8[i + u * stride] = quant8(v[u], s, r, exact_only);
+            for (int u = 0; u < kQuantUnroll; ++u) store_codes(&q8[i + u * stride], quant8(v[u], s, r, exact_only));
         }
-        for (; i < n16; i += stride) q8[i] = quant8(x16[i], s, r, exact_only);
+        for (; i < n16; i += stride) store_codes(&q8[i], quant8(x16[i], s, r, exact_only));
     }
     // the last numel % 8 elements, one per lane of workgroup 0
     if (blockIdx.x == 0) {
