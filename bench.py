@@ -104,7 +104,16 @@ def cpu_baseline(ci, cache_np, budget_s=12.0, clip=1.0):
     t_layer = t_quant + per_pos * total
     cnt = layer_counts(spec, cache_np is not None)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": cnt["ops"] / t_layer / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
             "sample": (f"absmax+quantize over all {spec.numel} elements ({t_quant:.2f} s) + conv/epilogue "
                        f"at {used} random output positions of {total} ({t_conv:.2f} s), scaled to the "
                        f"whole layer: {t_layer:.1f} s/layer")}
@@ -488,6 +497,8 @@ def main():
 
     # per kernel: K back-to-back launches each, on the launch stream
     _, conv_avg = timed(conv_pass, args.steps)
+    # the conv again in 5 groups of K/5 launches: median and min of the group averages
+    conv_groups = sorted(timed(conv_pass, max(1, args.steps // 5))[1] for _ in range(5))
     _, absmax_avg = timed(absmax_pass, args.steps)
     _, quant_avg = timed(quant_pass, args.steps)
     _, conv_mx_avg = timed(conv_absmax_pass, args.steps)
@@ -579,6 +590,14 @@ def main():
             "traffic": traffic,
             "algorithmic_ops_per_launch": cnt["ops"],
             "avg_launch_ms": round(conv_avg, 5),
+            "median_launch_ms": round(conv_groups[2], 5),
+            "min_launch_ms": round(conv_groups[0], 5),
+            "algorithmic_bytes_per_launch": cnt["conv_bytes"],
+            "ai_ops_per_byte": round(cnt["ops"] / cnt["conv_bytes"], 1),
+            # the attainable roofline min(MFMA peak, AI x HBM bandwidth) for this layer
+            "attainable_peak": round(min(PEAK_INT8_TOPS, cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 1),
+            "frac_of_attainable": round(conv_tops / min(PEAK_INT8_TOPS,
+                                                        cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 4),
         },
         "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
         "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),

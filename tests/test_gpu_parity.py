@@ -520,3 +520,28 @@ def test_layer_step_in_hip_graph(ops):
         other = ops.causalconv3d_w8a8(xq, xs, wq, ws, None)      # eager work between replays
         torch.cuda.synchronize()
         del other
+
+
+def test_layer_causality_end_to_end(ops):
+    """The GPU layer (absmax, quantize, conv): future frames changed under the
+    tensor maximum leave earlier frames' outputs bit-identical, with and without
+    a cache."""
+    g = torch.Generator().manual_seed(380)
+    N, T, H, W, C = 1, 6, 33, 40, 192
+    x = torch.randn(N, T, H, W, C, generator=g)
+    x[0, 0, 3, 4, 5] = 9.0
+    x2 = x.clone()
+    t0 = 2
+    x2[:, t0 + 1:] = (torch.rand(N, T - t0 - 1, H, W, C, generator=g) * 2 - 1) * 8.5
+    w = torch.randn(C, C, 3, 3, 3, generator=g) * 0.03
+    b = torch.randn(C, generator=g) * 0.01
+    wq, ws = ops.quantize_weights(w.to(DEV))
+    bd = b.to(DEV)
+    cache = torch.randint(-127, 128, (N, 2, H, W, C), generator=g, dtype=torch.int8).to(DEV)
+    for c in (None, cache):
+        y1, s1, _ = ops.layer_forward(to_dev_bits(_bits_of(x)).view(N, T, H, W, C), wq, ws, bd, c)
+        y2, s2, _ = ops.layer_forward(to_dev_bits(_bits_of(x2)).view(N, T, H, W, C), wq, ws, bd, c)
+        torch.cuda.synchronize()
+        assert f32_bits(s1.item()) == f32_bits(s2.item())
+        assert torch.equal(y1[:, :t0 + 1].view(torch.int16), y2[:, :t0 + 1].view(torch.int16))
+        assert not torch.equal(y1[:, t0 + 1:].view(torch.int16), y2[:, t0 + 1:].view(torch.int16))

@@ -642,3 +642,26 @@ def test_rmsnorm_silu_closed_form(oracle):
         expect = np.float32(ref).view(np.uint32)
         expect = (expect + 0x7FFF + ((expect >> 16) & 1)) >> 16        # bf16 round-to-nearest-even
         assert np.all(h == expect), (a, gam, h[0, 0], expect)
+
+
+def test_layer_causality_end_to_end(oracle):
+    """Whole layer (dynamic scale included): changing frames after t0 while keeping
+    every |x| below the tensor maximum (held in frame 0) leaves the outputs of
+    frames <= t0 unchanged, bit for bit."""
+    g = torch.Generator().manual_seed(28)
+    N, T, H, W, C = 1, 5, 6, 7, 32
+    x = torch.randn(N, T, H, W, C, generator=g)
+    x[0, 0, 0, 0, 0] = 8.0                                  # the maximum, in a past frame
+    x2 = x.clone()
+    t0 = 1
+    x2[:, t0 + 1:] = (torch.rand(N, T - t0 - 1, H, W, C, generator=g) * 2 - 1) * 7.5
+    xb = _bf16_bits_of(x)
+    xb2 = _bf16_bits_of(x2)
+    w = (torch.randn(C, C, 3, 3, 3, generator=g) * 0.05).numpy()
+    b = (torch.randn(C, generator=g) * 0.1).numpy()
+    wq, ws = oracle.quantize_weights(w)
+    y, s = oracle.layer(xb, wq, ws, b)
+    y2, s2 = oracle.layer(xb2, wq, ws, b)
+    assert s == s2
+    assert np.array_equal(y[:, :t0 + 1], y2[:, :t0 + 1])
+    assert not np.array_equal(y[:, t0 + 1:], y2[:, t0 + 1:])
