@@ -108,3 +108,46 @@ def test_rmsnorm_silu_rejects(ops):
     with pytest.raises(ops.QvaeError) as e:
         ops.rmsnorm_silu(torch.zeros(4, 512, dtype=torch.bfloat16, device=DEV), torch.ones(512, device=DEV))
     assert e.value.status == ops.EUNSUPPORTED
+
+
+def test_residual_branches_in_hip_graph(ops):
+    """Both residual branches captured once and replayed several times, with eager
+    work in between; every replay equals the eager result bit for bit."""
+    N, T, H, W, C = 1, 2, 23, 31, 96
+    xb, gamma = _draw(970, N * T * H * W, C, kind="normal")
+    g = torch.Generator().manual_seed(971)
+    w = (torch.randn(C, C, 3, 3, 3, generator=g) * 0.03).to(torch.bfloat16)
+    b = (torch.randn(C, generator=g) * 0.01).to(DEV)
+    x = to_dev_bits(xb).view(N, T, H, W, C)
+    gd = torch.from_numpy(gamma).to(DEV)
+    wq, ws = ops.quantize_weights(w.float().to(DEV))
+    wp = ops.pack_weights_bf16(w.to(DEV))
+    h = torch.empty_like(x)
+    am = torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=DEV)
+    xs = torch.empty((1,), dtype=torch.float32, device=DEV)
+    xq = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    y8 = torch.empty_like(x)
+    yn = torch.empty_like(x)
+    # eager references
+    he, ame = ops.rmsnorm_silu(x, gd, 1e-6, with_absmax=True)
+    xse, xqe = ops.act_quantize(he, ame)
+    y8e = ops.causalconv3d_w8a8(xqe, xse, wq, ws, b)
+    yne = ops.causalconv3d_bf16(ops.rmsnorm_silu(x, gd, 1e-6), wp, b)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ops.rmsnorm_silu(x, gd, 1e-6, out=h, absmax_bits=am, with_absmax=True)
+        ops.act_quantize(h, am, x_scale=xs, xq=xq)
+        ops.causalconv3d_w8a8(xq, xs, wq, ws, b, out=y8)
+        ops.rmsnorm_silu(x, gd, 1e-6, out=h)
+        ops.causalconv3d_bf16(h, wp, b, out=yn)
+    for rep in range(4):
+        y8.zero_()
+        yn.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y8.view(torch.int16), y8e.view(torch.int16)), f"W8A8 branch, replay {rep}"
+        assert torch.equal(yn.view(torch.int16), yne.view(torch.int16)), f"native branch, replay {rep}"
+        other = ops.rmsnorm_silu(x, gd, 0.5)                    # eager work between replays
+        torch.cuda.synchronize()
+        del other
