@@ -755,28 +755,43 @@ static int64_t px_tiles(const ConvArgs &a, int th, int tw)
 // Tile choice: the largest per-wave tile (3 x 4 blocks of 32x32 = 96 channels
 // x 128 pixels) whenever the channel count allows; split K inside the
 // workgroup when there are too few pixel tiles to give every CU a
-// workgroup.  1x1 kernels stage two slices per wave per stage when the slice
-// count allows it, so a stage still holds more than one k-step.
+// workgroup, but only while the split-K workgroups fit in one round of
+// resident workgroups (a second round would pay the fixed prologue and
+// epilogue again, and the full-K tiles then finish in one round anyway).
+// 1x1 kernels stage two slices per wave per stage when the slice count allows
+// it, so a stage still holds more than one k-step.
 template <int KH, int KW, int SPW>
 static int launch_spatial(const ConvArgs &a, int mode, hipStream_t st)
 {
     const int64_t cus = device_cus();
     const int S = a.Cin / 32;
     const bool k2 = S % (2 * SPW) == 0;   // the K range splits into two equal halves
+    const bool outmax = a.y_absmax != nullptr;
     if (a.Cout % 96 == 0) {
-        if (a.Cout % 384 == 0 && (px_tiles(a, 8, 16) * (a.Cout / 384) >= cus || !k2))
-            return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
-        if (a.Cout % 192 == 0 && (px_tiles(a, 16, 16) * (a.Cout / 192) >= cus || !k2))
-            return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
-        if (a.Cout % 192 == 0) return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
+        if (a.Cout % 384 == 0) {
+            const int64_t full = px_tiles(a, 8, 16) * (a.Cout / 384);
+            const int64_t split = px_tiles(a, 8, 16) * (a.Cout / 192);
+            if (full >= cus || !k2 ||
+                split > cus * resident_per_cu<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax))
+                return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
+        }
+        if (a.Cout % 192 == 0) {
+            const int64_t full = px_tiles(a, 16, 16) * (a.Cout / 192);
+            const int64_t split = px_tiles(a, 8, 16) * (a.Cout / 192);
+            if (full >= cus || !k2 ||
+                split > cus * resident_per_cu<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax))
+                return launch_cfg<2, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
+            return launch_cfg<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
+        }
+        const int64_t full = px_tiles(a, 16, 16) * (a.Cout / 96);
+        const bool split_fits =
+            k2 && px_tiles(a, 8, 16) * (a.Cout / 96) <= cus * resident_per_cu<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax);
         if constexpr (KH * KW > 1) {
             // 96 channels: memory-bound; 96x64 wave tiles keep two workgroups
             // per CU so one's loads and stores overlap the other's MFMAs
-            if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
-                return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, mode, st);
+            if (full >= cus || !split_fits) return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, mode, st);
         } else {
-            if (px_tiles(a, 16, 16) * (a.Cout / 96) >= cus || !k2)
-                return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
+            if (full >= cus || !split_fits) return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
         }
         return launch_cfg<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
     }
