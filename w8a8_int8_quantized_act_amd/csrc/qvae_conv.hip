@@ -788,7 +788,11 @@ static int launch_spatial(const ConvArgs &a, int mode, hipStream_t st)
             k2 && px_tiles(a, 8, 16) * (a.Cout / 96) <= cus * resident_per_cu<1, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax);
         if constexpr (KH * KW > 1) {
             // 96 channels: memory-bound; 96x64 wave tiles keep two workgroups
-            // per CU so one's loads and stores overlap the other's MFMAs
+            // per CU so one's loads and stores overlap the other's MFMAs.  The
+            // bf16 conv (twice the operand bytes per MFMA) does better with
+            // 96x128 wave tiles, which halve the weight loads per pixel, once the
+            // frame has a tile for every CU.
+            if (mode == kModeBf16 && full >= cus) return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
             if (full >= cus || !split_fits) return launch_cfg<1, 4, 1, 3, 2, 16, 16, KH, KW, SPW>(a, mode, st);
         } else {
             if (full >= cus || !split_fits) return launch_cfg<1, 2, 1, 3, 4, 16, 16, KH, KW, SPW>(a, mode, st);
