@@ -12,7 +12,14 @@
  *     rescale, output in the activation's precision;
  *   - same section, fixed-parameter paragraph: clip ratio 1.0 for activations
  *     and weights, channels_last layout, automatic fallback to native
- *     precision on error.
+ *     precision on error;
+ *   - same section, the preset list and the exclusion rule: which of the
+ *     decoder's 28 patched Conv3d layers run in W8A8, the others staying in
+ *     native precision (qvae_select_layer, qvae_causalconv3d_bf16).
+ * Around the convolution: the RMSNorm + SiLU pass that feeds a decoder
+ * residual conv, with the activation maximum fused in (qvae_rmsnorm_silu*;
+ * page "Doubling LLM token rates in ComfyUI", section "Optimizing linear
+ * kernels": activation quantization absorbing the preceding RMSNorm).
  * Readings where the page is silent: the activation scale is one scale per
  * tensor, s = fl(clip * absmax) / 127; codes are round-half-to-even of the
  * IEEE float32 quotient x / s, clamped to [-127, 127] (0 when s == 0); the
@@ -27,7 +34,7 @@
  *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronize with the host;
  *   - layouts are channels-last: activations [N][T][H][W][C], contiguous;
- *   - x, xq, wq, y, acc and cache must be 16-byte aligned;
+ *   - x, xq, wq, wp, h, y, acc and cache must be 16-byte aligned;
  *   - the return value is a status code (QVAE_OK = 0, negative on error);
  *     arguments are validated before anything is launched; the library never
  *     aborts or throws; on a non-zero status the caller is expected to fall
@@ -53,7 +60,7 @@ extern "C" {
 #define QVAE_EINVAL (-1)       /* null pointer, bad size, misaligned buffer   */
 #define QVAE_EUNSUPPORTED (-2) /* valid but outside the supported set          */
 #define QVAE_ELAUNCH (-3)      /* the HIP runtime reported a launch error      */
-#define QVAE_EFORCED (-4)      /* QVAE_FORCE_FAIL=1 is set                     */
+#define QVAE_EFORCED (-4)      /* failure forced by QVAE_FORCE_FAIL            */
 
 /* Library version, (major << 16) | minor. */
 int qvae_version(void);

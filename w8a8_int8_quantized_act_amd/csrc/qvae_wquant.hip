@@ -134,7 +134,7 @@ extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, 
     return launch_status();
 }
 
-extern "C" int qvae_version(void) { return (0 << 16) | 1; }
+extern "C" int qvae_version(void) { return (0 << 16) | 2; }
 
 extern "C" const char *qvae_strerror(int status)
 {
