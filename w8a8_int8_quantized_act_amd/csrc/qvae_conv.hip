@@ -47,6 +47,13 @@
 // through LDS, so every lane stores 16 contiguous bytes of the channels-last
 // output; on request it also reduces the maximum of |y| into one partial slot
 // per workgroup (the next layer's activation maximum).
+//
+// The same kernel, compiled with bf16 operands, is the native-precision conv
+// of the layers a preset leaves unquantized (same section, the preset list):
+// y = bf16_rne(fl32(sum of bf16 x bf16 products) + bias[co]), the sum in the
+// matrix cores' FP32 accumulation order.  Everything above moves bytes, so
+// that variant only swaps the matrix instruction (32x32x16 bf16, the same 16
+// bytes per lane and operand) and the epilogue's rescale.
 #include <type_traits>
 #include <utility>
 
