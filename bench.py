@@ -213,6 +213,50 @@ def operand_probe(args):
     print(json.dumps(out))
 
 
+def decoder_cpu_baseline(data, budget_s=12.0):
+    """The oracle (as it stands) on the native residual branches of the stack:
+    RMSNorm + SiLU over one layer's whole input and the exact bf16 conv at a
+    random sample of output positions, per distinct layer shape, scaled to all
+    28 layers (ms per stack)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    shapes = {}
+    for d in data:
+        s = d["spec"]
+        shapes.setdefault((s.Cin, s.Cout, s.H, s.W), []).append(d)
+    per_shape_budget = budget_s / len(shapes)
+    total_s = 0.0
+    notes = []
+    rng = np.random.default_rng(0)
+    for (cin, cout, h, w), ds in shapes.items():
+        d = ds[0]
+        xb = d["x"].view(torch.int16).cpu().numpy().view(np.uint16)
+        gam = d["gam"].cpu().numpy()
+        wb = d["w"].view(torch.int16).cpu().numpy().view(np.uint16)
+        b = d["b"].cpu().numpy()
+        t0 = time.perf_counter()
+        hb = oracle.rmsnorm_silu(xb, gam, 1e-6)
+        t_norm = time.perf_counter() - t0
+        npos, t_conv, used = 16, 0.0, 0
+        while t_conv < per_shape_budget * 0.8 and used < h * w:
+            pos = rng.integers(0, h * w, npos).astype(np.int64)
+            t0 = time.perf_counter()
+            oracle.conv_bf16(hb, wb, b, positions=pos)
+            t_conv += time.perf_counter() - t0
+            used += npos
+            npos *= 2
+        layer_s = t_norm + t_conv / used * h * w
+        total_s += layer_s * len(ds)
+        notes.append(f"{cin}->{cout} @{h}x{w}: norm {t_norm:.2f} s + conv at {used} of {h * w} positions "
+                     f"{t_conv:.2f} s -> {layer_s:.1f} s/layer x {len(ds)}")
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    return {"value": round(total_s * 1e3, 1), "unit": "ms per stack (native residual branches)", "cores": threads,
+            "kind": "oracle", "sample": "; ".join(notes)}
+
+
 def decoder_stack(args):
     """The 28 residual-block convs of the decoder at one output size, run as
     each preset says (W8A8 layer step = absmax + quantize + INT8 conv, native =
@@ -238,7 +282,7 @@ def decoder_stack(args):
         wq, ws = ops.quantize_weights(w.float())
         wp = ops.pack_weights_bf16(w)
         gam = (1.0 + 0.1 * torch.randn(spec.Cin, generator=g, device=dev)).float()
-        d = dict(spec=spec, x=x, b=b, wq=wq, ws=ws, wp=wp, gam=gam,
+        d = dict(spec=spec, x=x, b=b, w=w, wq=wq, ws=ws, wp=wp, gam=gam,
                  hb=torch.empty(x.shape, dtype=torch.bfloat16, device=dev),
                  xq=torch.empty(x.shape, dtype=torch.int8, device=dev),
                  xs=torch.empty((1,), dtype=torch.float32, device=dev),
@@ -333,7 +377,9 @@ def decoder_stack(args):
                        "norm_silu_ms": round(norm, 5), "norm_silu_GBs": round(nbytes / (norm * 1e-3) / 1e9, 1),
                        "norm_silu_absmax_ms": round(norm_mx, 5), "quantize_ms": round(quant, 5),
                        "branch_native_ms": round(norm + nat, 5), "branch_w8a8_ms": round(norm_mx + quant + conv, 5)}
+    cpu = None if args.no_cpu else decoder_cpu_baseline(data, args.cpu_budget)
     print(json.dumps({"probe": "decoder conv stack by preset", "output": f"{args.out_h}x{args.out_w}",
+                      "cpu_baseline": cpu,
                       "layers": len(layers), "alg_GOP_per_stack": round(total_ops / 1e9, 1),
                       "steps": args.steps, "presets": presets, "residual_branches": branches, "per_shape": shapes,
                       "note": "presets: W8A8 layer = absmax + quantize + INT8 conv, native layer = bf16 conv "
