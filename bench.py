@@ -310,6 +310,12 @@ def decoder_stack(args):
                         (L.qvae_causalconv3d_w8a8, (P(d["xq"].data_ptr()), P(d["xs"].data_ptr()), None,
                                                     P(wq.data_ptr()), P(ws.data_ptr()), P(b.data_ptr()), *dims,
                                                     P(d["y"].data_ptr()), sp))]
+        # the branch with the quantize pass absorbed into the conv (it reads bf16 h)
+        d["br_w8a8_qin"] = [d["br_w8a8"][0],
+                            (L.qvae_causalconv3d_w8a8_qin, (hp, None, P(d["am"].data_ptr()), ctypes.c_float(1.0),
+                                                            P(wq.data_ptr()), P(ws.data_ptr()), P(b.data_ptr()),
+                                                            *dims, P(d["xs"].data_ptr()), P(d["y"].data_ptr()), sp))]
+        d["qin_ok"] = spec.H * spec.W >= decoder.QIN_MIN_PIXELS
         # the same branch without the fused maximum: norm + SiLU, then both quantizer passes
         d["br_w8a8_unfused"] = [d["br_native"][0]] + [
             (f, (hp,) + a[1:]) for f, a in d["w8a8"][:2]] + d["br_w8a8"][2:]
@@ -344,10 +350,17 @@ def decoder_stack(args):
     # whole residual branches (norm + SiLU + conv) per preset; W8A8 layers with
     # the maximum fused into the norm pass, and (for Aggressive) without it
     branches = {}
+    def branch(d, key):
+        if key == "qin":   # the input-quantizing conv where the runner's rule picks it
+            return d["br_w8a8_qin"] if d["qin_ok"] else d["br_w8a8"]
+        return d[key]
+
     for preset, key in (("native", "br_w8a8"), ("conservative", "br_w8a8"), ("balanced", "br_w8a8"),
-                        ("aggressive", "br_w8a8"), ("aggressive_unfused_absmax", "br_w8a8_unfused")):
+                        ("aggressive", "br_w8a8"), ("aggressive_unfused_absmax", "br_w8a8_unfused"),
+                        ("conservative_quantize_in_conv", "qin"), ("balanced_quantize_in_conv", "qin"),
+                        ("aggressive_quantize_in_conv", "qin")):
         pl = decoder.plan(preset.split("_")[0], layers)
-        calls = [c for d in data for c in (d[key] if pl[d["spec"].name] else d["br_native"])]
+        calls = [c for d in data for c in (branch(d, key) if pl[d["spec"].name] else d["br_native"])]
         timed(calls, 2)
         ms = float(np.median([timed(calls, args.steps) for _ in range(3)]))
         branches[preset] = {"w8a8_layers": sum(pl.values()), "ms_per_stack": round(ms, 4)}
@@ -364,6 +377,7 @@ def decoder_stack(args):
         nat = timed(d["native"], args.steps)
         step = timed(d["w8a8"], args.steps)
         conv = timed(d["w8a8"][2:], args.steps)
+        qin = timed(d["br_w8a8_qin"][1:], args.steps)
         norm = timed(d["br_native"][:1], args.steps)
         norm_mx = timed(d["br_w8a8"][:1], args.steps)
         quant = timed(d["br_w8a8"][1:2], args.steps)
@@ -376,7 +390,8 @@ def decoder_stack(args):
                        "w8a8_conv_frac_of_int8_peak": round(d["ops"] / (conv * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                        "norm_silu_ms": round(norm, 5), "norm_silu_GBs": round(nbytes / (norm * 1e-3) / 1e9, 1),
                        "norm_silu_absmax_ms": round(norm_mx, 5), "quantize_ms": round(quant, 5),
-                       "branch_native_ms": round(norm + nat, 5), "branch_w8a8_ms": round(norm_mx + quant + conv, 5)}
+                       "branch_native_ms": round(norm + nat, 5), "branch_w8a8_ms": round(norm_mx + quant + conv, 5),
+                       "conv_quantize_in_ms": round(qin, 5), "branch_w8a8_qin_ms": round(norm_mx + qin, 5)}
     cpu = None if args.no_cpu else decoder_cpu_baseline(data, args.cpu_budget)
     print(json.dumps({"probe": "decoder conv stack by preset", "output": f"{args.out_h}x{args.out_w}",
                       "cpu_baseline": cpu,
@@ -385,7 +400,8 @@ def decoder_stack(args):
                       "note": "presets: W8A8 layer = absmax + quantize + INT8 conv, native layer = bf16 conv "
                               "(FP32 accumulation); residual_branches: each conv preceded by its RMSNorm + SiLU "
                               "pass (native: norm + SiLU -> bf16 conv; W8A8: norm + SiLU with the fused maximum -> "
-                              "quantize -> INT8 conv); each layer has its own resident input; HIP events around "
+                              "quantize -> INT8 conv; *_quantize_in_conv: the conv quantizes h itself on frames of "
+                              f"at least {decoder.QIN_MIN_PIXELS} pixels); each layer has its own resident input; HIP events around "
                               "K back-to-back stacks, median of 3"}))
 
 

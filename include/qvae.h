@@ -277,6 +277,31 @@ int qvae_causalconv3d_bf16(const uint16_t *x, const uint16_t *cache, const uint1
                            void *stream);
 
 /*
+ * qvae_causalconv3d_w8a8 on bf16 input: the conv quantizes x (and the cache)
+ * itself as it stages them, so no quantize pass runs in between (the
+ * activation quantizer absorbed into its consumer).  Codes, scale and output
+ * are exactly those of qvae_act_quantize on x (and on the cache, with the same
+ * scale) followed by qvae_causalconv3d_w8a8.
+ *   x         bf16 bit patterns [N][T][H][W][Cin]
+ *   cache     bf16 bit patterns [N][kt-1][H][W][Cin] (the kt-1 frames before
+ *             frame 0, oldest first) or NULL = zero front frames
+ *   x_absmax  activation-maximum buffer (QVAE_ABSMAX_WORDS words) whose words
+ *             1.. hold partial maxima of |x| and of the cache (from
+ *             qvae_act_absmax, qvae_causalconv3d_w8a8_absmax or
+ *             qvae_rmsnorm_silu_absmax over the tensor they belong to); word 0
+ *             is written with the maximum
+ *   clip_ratio  0 < clip_ratio <= 1, as for qvae_act_quantize
+ *   x_scale   float32 [1] out (the scale used), or NULL
+ *   y         bf16 bit patterns [N][T][H][W][Cout] out
+ * Same support as qvae_causalconv3d_w8a8; x_absmax == NULL or clip_ratio <= 0 /
+ * NaN is QVAE_EINVAL.
+ */
+int qvae_causalconv3d_w8a8_qin(const uint16_t *x, const uint16_t *cache, uint32_t *x_absmax, float clip_ratio,
+                               const int8_t *wq, const float *w_scale, const float *bias, int N, int T, int H,
+                               int W, int Cin, int Cout, int kt, int kh, int kw, float *x_scale, uint16_t *y,
+                               void *stream);
+
+/*
  * Same contraction, writing the raw INT32 accumulators instead of the
  * epilogue (a verification export):
  *   acc  int32 [N][T][H][W][Cout] out

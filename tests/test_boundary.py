@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ["qvae_quantize_weights", "qvae_act_absmax", "qvae_act_quantize", "qvae_act_absmax_quant",
               "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_absmax", "qvae_causalconv3d_w8a8_acc32",
               "qvae_select_layer", "qvae_pack_weights_bf16", "qvae_causalconv3d_bf16",
-              "qvae_rmsnorm_silu", "qvae_rmsnorm_silu_absmax",
+              "qvae_rmsnorm_silu", "qvae_rmsnorm_silu_absmax", "qvae_causalconv3d_w8a8_qin",
               "qvae_strerror", "qvae_version"]:
         assert n in names
 
@@ -138,6 +138,21 @@ def test_bf16_entry_points_reject(L):
     assert p(FAKE, 32, 24, 3, 3, 3, FAKE, None) == -2
 
 
+def test_conv_qin_rejects(L):
+    f = L.qvae_causalconv3d_w8a8_qin
+    dims = (1, 1, 4, 4, 32, 32, 3, 3, 3)
+    assert f(FAKE, None, None, 1.0, FAKE, FAKE, None, *dims, None, FAKE, None) == -1        # no maximum buffer
+    assert f(FAKE, None, FAKE, 0.0, FAKE, FAKE, None, *dims, None, FAKE, None) == -1        # clip 0
+    assert f(FAKE, None, FAKE, float("nan"), FAKE, FAKE, None, *dims, None, FAKE, None) == -1
+    assert f(FAKE, None, FAKE, 1.5, FAKE, FAKE, None, *dims, None, FAKE, None) == -2        # clip > 1
+    assert f(FAKE, None, FAKE, 1.0, FAKE, None, None, *dims, None, FAKE, None) == -1        # no weight scales
+    assert f(FAKE_MIS, None, FAKE, 1.0, FAKE, FAKE, None, *dims, None, FAKE, None) == -1
+    assert f(FAKE, FAKE_MIS, FAKE, 1.0, FAKE, FAKE, None, *dims, None, FAKE, None) == -1
+    assert f(FAKE, None, FAKE, 1.0, FAKE, FAKE, None, 1, 1, 4, 4, 48, 32, 3, 3, 3, None, FAKE, None) == -2
+    assert f(FAKE, None, FAKE, 1.0, FAKE, FAKE, None, 1, 1, 4, 4, 32, 40, 3, 3, 3, None, FAKE, None) == -2
+    assert f(FAKE, None, FAKE, 1.0, FAKE, FAKE, None, 1, 1, 4, 4, 4960, 32, 3, 3, 3, None, FAKE, None) == -2
+
+
 def test_rmsnorm_silu_rejects(L):
     f, fa = L.qvae_rmsnorm_silu, L.qvae_rmsnorm_silu_absmax
     assert f(None, 4, 96, FAKE, 1e-6, FAKE, None) == -1
@@ -180,11 +195,12 @@ def test_force_fail_w8a8_only():
         "      L.qvae_act_quantize(F, 16, 1.0, F, F, F, None),\n"
         "      L.qvae_quantize_weights(F, 32, 32, 3, 3, 3, 1.0, F, F, None),\n"
         "      L.qvae_causalconv3d_w8a8(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
-        "      L.qvae_causalconv3d_w8a8_absmax(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, F, None)]\n"
+        "      L.qvae_causalconv3d_w8a8_absmax(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, F, None),\n"
+        "      L.qvae_causalconv3d_w8a8_qin(F, None, F, 1.0, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, None, F, None)]\n"
         "nat = [L.qvae_causalconv3d_bf16(M, None, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
         "       L.qvae_pack_weights_bf16(F, 32, 32, 3, 3, 3, M, None)]\n"
         "sel = L.qvae_select_layer(3, b'decoder.middle.0.residual.2', 384, 384, 3, 3, 3, 384)\n"
-        "sys.exit(0 if w8 == [-4] * 5 and nat == [-1, -1] and sel == 1 else 1)\n")
+        "sys.exit(0 if w8 == [-4] * 6 and nat == [-1, -1] and sel == 1 else 1)\n")
     env = dict(os.environ, QVAE_FORCE_FAIL="w8a8")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr

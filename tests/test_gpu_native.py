@@ -162,6 +162,17 @@ def test_runner_follows_the_plan(ops, stack, preset, count):
     assert n_w8a8 == count
 
 
+def test_runner_quantize_in_conv_equals_two_step(ops, stack):
+    # the input-quantizing conv gives the runner's W8A8 layers bit-identical results
+    for L, w, b, x in stack[:12]:
+        two = decoder.PlannedConv(L.name, w, b, "balanced", quantize_in_conv=False)
+        one = decoder.PlannedConv(L.name, w, b, "balanced", quantize_in_conv=True)
+        assert two.w8a8 == one.w8a8
+        y2, y1 = two(x), one(x)
+        torch.cuda.synchronize()
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16)), L.name
+
+
 def test_runner_w8a8_layer_against_the_oracle(ops, stack):
     L, w, b, x = stack[10]                     # decoder.upsamples.4.residual.2, 192 -> 384 @ 32x32
     conv = decoder.PlannedConv(L.name, w, b, "balanced")

@@ -72,7 +72,10 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 //   kModeAcc32  W8A8, raw INT32 accumulators
 //   kModeBf16   bf16 x bf16 products, FP32 accumulation, y = bf16_rne(acc + bias)
 //               (the native-precision conv for the layers left unquantized)
-constexpr int kModePlain = 0, kModeAcc32 = 1, kModeBf16 = 2;
+//   kModeQin    W8A8 from bf16 input: the conv quantizes x (and the cache) as it
+//               stages the halo, with the scale it reduces from the partial
+//               maxima of x in its prologue (no separate quantize pass)
+constexpr int kModePlain = 0, kModeAcc32 = 1, kModeBf16 = 2, kModeQin = 3;
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>): the index
 // is a compile-time constant in every call, so arrays it selects from stay in
@@ -101,6 +104,9 @@ struct ConvArgs {
     uint32_t *y_absmax;     // partial-maximum slots of the output's |y|, or NULL
     int co_tiles, T, H, W, Cin, Cout, kt, N;
     int tiles_w, tiles_h;
+    uint32_t *x_absmax;     // input-quantizing conv: activation-maximum buffer of x (words 1.. read, word 0 written)
+    float *x_scale_out;     // input-quantizing conv: the scale it used, or NULL
+    float clip;             // input-quantizing conv: clip ratio
 };
 
 // Cache policy of the output stores: non-temporal (the output is not read
@@ -168,11 +174,17 @@ struct ConvCfg {
 // 2 x the channels, so a 32-byte slice holds 16 channels and one 16-byte lane
 // fragment feeds the bf16 matrix instruction exactly as it feeds the INT8
 // one), FP32 accumulators, y = bf16_rne(fma(acc, 1, bias)).
+// QIN: the input (and the cache) are bf16; every halo chunk of 16 channels is
+// loaded as 32 bytes and quantized to codes before it is staged, exactly as
+// the quantize pass would code it, with the scale s = fl(clip * max|x|) / 127
+// reduced from x's partial maxima in the prologue.
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32, bool OUTMAX,
-          bool BF>
+          bool BF, bool QIN>
 __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 1) void k_conv_igemm(ConvArgs a)
 {
     static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
+    static_assert(!(QIN && (ACC32 || OUTMAX || BF)), "the input-quantizing conv has the plain epilogue only");
+    constexpr int XB = QIN ? 2 : 1;   // bytes per input value in global memory
     using AccV = std::conditional_t<BF, v16f, v16i>;
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
     constexpr int NT = C::NT;
@@ -193,6 +205,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     asm volatile("" ::"s"(a.wq), "s"(a.x_scale), "s"(a.w_scale), "s"(a.bias), "s"(a.xq), "s"(a.cache), "s"(a.out),
                  "s"(a.co_tiles), "s"(a.T), "s"(a.H), "s"(a.W), "s"(a.Cin), "s"(a.Cout), "s"(a.kt), "s"(a.N),
                  "s"(a.tiles_w), "s"(a.tiles_h), "s"(a.y_absmax));
+    if constexpr (QIN) asm volatile("" ::"s"(a.x_absmax), "s"(a.x_scale_out), "s"(a.clip));
     // ---- tiles.  Pixel tiles are numbered pt = column + tiles_w * (row +
     // tiles_h * (t + T * n)).  Workgroup b runs channel tile b % co_tiles and
     // pixel tiles b / co_tiles + k * (gridDim.x / co_tiles), k = 0, 1, ...
@@ -271,8 +284,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     float *s_fac = reinterpret_cast<float *>(smem + WORK);
     float f_ws[FPT], f_b[FPT];
     float sx = 0.0f;
+    uint32_t qmax = 0;   // QIN: this thread's share of x's partial maxima
+    if constexpr (QIN) {
+        for (int k = tid; k < kAbsmaxParts; k += NT) qmax = max(qmax, a.x_absmax[1 + k]);
+    }
     if constexpr (!ACC32) {
-        sx = BF ? 1.0f : *a.x_scale;
+        sx = (BF || QIN) ? 1.0f : *a.x_scale;
 #pragma unroll
         for (int k = 0; k < FPT; ++k) {
             const int c = tid + k * NT;
@@ -311,7 +328,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                 const int q = u / (2 * C::SL), c = u - q * (2 * C::SL);
                 const int hh = q / C::HWD, ww = q - hh * C::HWD;
                 const int gh = tl.h0 - PH + hh, gw = tl.w0 - PW + ww;
-                if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (uint32_t)((gh * W + gw) * Cin + c * 16);
+                if (gh >= 0 && gh < H && gw >= 0 && gw < W) h_off[k] = (uint32_t)(((gh * W + gw) * Cin + c * 16) * XB);
             }
         }
     };
@@ -324,25 +341,46 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             h_lds[k] = (c >> 1) * C::SLICE_BYTES + q * kHaloPitch + (c & 1) * 16;
         }
     }
-    const size_t frame_bytes = (size_t)H * W * Cin;
+    const size_t frame_bytes = (size_t)H * W * Cin * XB;   // bytes of one input frame in global memory
     auto frame_ptr = [&](const Tile &tl, int i) -> const int8_t * {
         const int tau = tl.t - (kt - 1) + i;
         if (tau >= 0) return a.xq + ((size_t)tl.n * a.T + tau) * frame_bytes;
         return a.cache + ((size_t)tl.n * (kt - 1) + (kt - 1 + tau)) * frame_bytes;
     };
     v4i hreg[C::HALO_PT];
+    v4i hreg2[QIN ? C::HALO_PT : 1];   // QIN: the second 16 bytes (channels 8..15) of each bf16 chunk
     auto halo_rsrc = [&](const Tile &tl, int st) {
         const int it = st / nsp;
         const int p = st - it * nsp;
-        const int8_t *fps = frame_ptr(tl, tl.i_lo + it) + p * C::SL * 32;
+        const int8_t *fps = frame_ptr(tl, tl.i_lo + it) + p * C::SL * 32 * XB;
         return __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t *>(fps), 0,
-                                                 (int)(frame_bytes - (size_t)p * C::SL * 32), 0x00020000);
+                                                 (int)(frame_bytes - (size_t)p * C::SL * 32 * XB), 0x00020000);
     };
     auto load_chunk = [&](__amdgpu_buffer_rsrc_t rs, int k) {
         hreg[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)h_off[k], 0, 0));
+        if constexpr (QIN)   // (an out-of-image pixel's offset + 16 is still past the buffer)
+            hreg2[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(h_off[k] + 16), 0, 0));
+    };
+    // QIN: the scale of x and the quantizer's constants (set in the prologue)
+    float q_s = 0.0f, q_r = 0.0f;
+    bool q_zero = true, q_exact = false;
+    auto quant_half = [&](v4i v) -> uint2 {
+        return q_zero ? make_uint2(0u, 0u) : quant8(__builtin_bit_cast(u32x4, v), q_s, q_r, q_exact);
+    };
+    auto store_codes_lds = [&](int buf, int k, uint2 c0, uint2 c1) {
+        *reinterpret_cast<v4i *>(smem + buf * C::BUF_BYTES + h_lds[k]) = v4i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
     };
     auto store_chunk = [&](int buf, int k) {
-        *reinterpret_cast<v4i *>(smem + buf * C::BUF_BYTES + h_lds[k]) = hreg[k];
+        v4i v = hreg[k];
+        if constexpr (QIN) {
+            v = v4i{0, 0, 0, 0};
+            if (!q_zero) {
+                const uint2 c0 = quant8(__builtin_bit_cast(u32x4, hreg[k]), q_s, q_r, q_exact);
+                const uint2 c1 = quant8(__builtin_bit_cast(u32x4, hreg2[k]), q_s, q_r, q_exact);
+                v = v4i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+            }
+        }
+        *reinterpret_cast<v4i *>(smem + buf * C::BUF_BYTES + h_lds[k]) = v;
     };
     auto load_halo = [&](const Tile &tl, int st) {
         const __amdgpu_buffer_rsrc_t rs = halo_rsrc(tl, st);
@@ -357,6 +395,28 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     set_hoff(cur);
     load_halo(cur, 0);
     __builtin_amdgcn_sched_barrier(0);
+
+    // QIN: the tensor maximum from the partial maxima (while the first halo is
+    // in flight), then the scale the quantize pass would derive from it
+    if constexpr (QIN) {
+        __shared__ uint32_t s_qmax[C::NW];
+        const uint32_t m = wave_max_u32(qmax);
+        if (lane == 0) s_qmax[wave] = m;
+        lds_barrier();
+        uint32_t mbits = s_qmax[0];
+#pragma unroll
+        for (int k = 1; k < C::NW; ++k) mbits = max(mbits, s_qmax[k]);
+        const float amax = bf16_bits_to_float(mbits);
+        q_s = (a.clip * amax) / 127.0f;
+        q_r = 1.0f / q_s;
+        q_zero = !(q_s > 0.0f);
+        q_exact = !(q_r < __builtin_inff());
+        sx = q_s;
+        if (blockIdx.x == 0 && tid == 0) {
+            a.x_absmax[0] = mbits;
+            if (a.x_scale_out) *a.x_scale_out = q_s;
+        }
+    }
 
     // B fragment base offsets (pixel of lane, within the stage buffer)
     int b_q0[NB];
@@ -432,6 +492,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
 #pragma unroll
         for (int e = 0; e < C::KS; ++e) {
             const int slot = e % C::PD;
+            uint2 qc0 = make_uint2(0u, 0u);   // QIN: first half of the chunk being staged this step
             const bool wload = e + C::PD < C::KS || MORE == 2;
             const int wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024 : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
@@ -460,7 +521,17 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                         constexpr int hl = NB < last ? NB : last;
                         constexpr int hs = NB + 1 < last ? NB + 1 : last;
                         if (i == hl && e < C::HALO_PT) load_chunk(rsn, e);
-                        if (i == hs && e >= C::PD && e - C::PD < C::HALO_PT) store_chunk(buf ^ 1, e - C::PD);
+                        if constexpr (QIN) {
+                            // the two 8-value halves of the chunk are quantized in two
+                            // consecutive MFMA slots, so neither burst stalls the matrix pipe long
+                            constexpr int hs2 = hs + 1 <= last ? hs + 1 : hs;
+                            if (e >= C::PD && e - C::PD < C::HALO_PT) {
+                                if (i == hs) qc0 = quant_half(hreg[e - C::PD]);
+                                if (i == hs2) store_codes_lds(buf ^ 1, e - C::PD, qc0, quant_half(hreg2[e - C::PD]));
+                            }
+                        } else {
+                            if (i == hs && e >= C::PD && e - C::PD < C::HALO_PT) store_chunk(buf ^ 1, e - C::PD);
+                        }
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -699,12 +770,19 @@ template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int 
 static const void *conv_kernel(int mode, bool outmax)
 {
     if (mode == kModeAcc32)
-        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false, false>);
+        return reinterpret_cast<const void *>(
+            &k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, true, false, false, false>);
     if (mode == kModeBf16)
-        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, true>);
+        return reinterpret_cast<const void *>(
+            &k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, true, false>);
+    if (mode == kModeQin)
+        return reinterpret_cast<const void *>(
+            &k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, false, true>);
     if (outmax)
-        return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true, false>);
-    return reinterpret_cast<const void *>(&k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, false>);
+        return reinterpret_cast<const void *>(
+            &k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, true, false, false>);
+    return reinterpret_cast<const void *>(
+        &k_conv_igemm<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, false, false, false, false>);
 }
 
 // Workgroups of one instantiation that fit on a CU at once (registers, LDS,
@@ -713,8 +791,8 @@ template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int 
 static int resident_per_cu(int mode, bool outmax)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
-    static int occ[4] = {0, 0, 0, 0};
-    const int v = (mode == kModePlain && outmax) ? 3 : mode;
+    static int occ[5] = {0, 0, 0, 0, 0};
+    const int v = (mode == kModePlain && outmax) ? 4 : mode;
     int &o = occ[v];
     if (o == 0) {
         int n = 0;
@@ -927,4 +1005,32 @@ extern "C" int qvae_causalconv3d_bf16(const uint16_t *x, const uint16_t *cache, 
     a.out = y;
     a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = 2 * Cin, a.Cout = Cout, a.kt = kt;
     return conv_dispatch(a, kh, kModeBf16, as_stream(stream));
+}
+
+extern "C" int qvae_causalconv3d_w8a8_qin(const uint16_t *x, const uint16_t *cache, uint32_t *x_absmax,
+                                          float clip_ratio, const int8_t *wq, const float *w_scale,
+                                          const float *bias, int N, int T, int H, int W, int Cin, int Cout, int kt,
+                                          int kh, int kw, float *x_scale, uint16_t *y, void *stream)
+{
+    if (force_fail(true)) return QVAE_EFORCED;
+    if (!x_absmax || !w_scale) return QVAE_EINVAL;
+    if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;
+    if (clip_ratio > 1.0f) return QVAE_EUNSUPPORTED;
+    int rc = conv_validate(x, wq, y, N, T, H, W, Cin, Cout, kt, kh, kw, cache, 2 * (int64_t)Cin, 4);
+    if (rc != QVAE_OK) return rc;
+    if (Cin % 32 != 0) return QVAE_EUNSUPPORTED;
+    const int64_t K = (int64_t)Cin * kt * kh * kw;
+    if (K * 127 * 127 >= ((int64_t)1 << 31)) return QVAE_EUNSUPPORTED;
+    ConvArgs a{};
+    a.xq = reinterpret_cast<const int8_t *>(x);
+    a.cache = (kt > 1) ? reinterpret_cast<const int8_t *>(cache) : nullptr;
+    a.wq = wq;
+    a.w_scale = w_scale;
+    a.bias = bias;
+    a.out = y;
+    a.x_absmax = x_absmax;
+    a.x_scale_out = x_scale;
+    a.clip = clip_ratio;
+    a.N = N, a.T = T, a.H = H, a.W = W, a.Cin = Cin, a.Cout = Cout, a.kt = kt;
+    return conv_dispatch(a, kh, kModeQin, as_stream(stream));
 }

@@ -101,6 +101,82 @@ __device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t w)
     return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
 }
 
+// ---- the activation quantizer's codes (shared by the quantize pass and the
+// conv that quantizes its own bf16 input) ------------------------------------
+//
+// The quotient x / s is the IEEE binary32 one.  The fast path computes
+// t = x * r with r = fl(1 / s) and keeps rne(t) when t is far from a rounding
+// boundary: |fl(x*r) - x/s| <= |x/s| * (2^-23 + 2^-46) and
+// |fl(x/s) - x/s| <= |x/s| * 2^-24, so when t is more than |t| * 2^-20 away from
+// every half-integer, t and fl(x/s) round to the same integer.  Otherwise (and
+// whenever 1/s is not finite) the group is redone with the correctly rounded
+// division.  A scale of 0 is the caller's case (every code 0).
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// One activation code by the definition: clamp(rne(fl(x / s)), -127, 127).
+__device__ __forceinline__ int quant_code_exact(float x, float s)
+{
+    const float n = __builtin_rintf(x / s);
+    return (int)fminf(fmaxf(n, -127.0f), 127.0f);
+}
+
+// Fast path for 8 bf16 values (one 16-byte load) -> 8 codes (two words).
+//   t  = med3(x * r, -127, 127)     clamping first is exact: the code of any
+//                                   |x/s| >= 127 is +-127 either way, and a
+//                                   clamped t sits 0.5 from every boundary
+//   m  = t + 1.5 * 2^23             rounds t to an integer (round to nearest
+//                                   even); the low byte of m's bits is the
+//                                   two's-complement code
+//   d  = |t - (m - 1.5 * 2^23)| - 0.5   minus the distance to the nearest half-integer
+//   f  = |d| - |t| * 2^-20           negative when t is too close to a rounding
+//                                   boundary for fl(x * r) to stand in for fl(x / s)
+// The smallest f of the 8 values is returned in fmin; the caller redoes the
+// whole group exactly when it is not positive.
+__device__ __forceinline__ uint2 quant8_fast(u32x4 v, float r, float &fmin)
+{
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    uint32_t code[8];
+    float f = 1.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t w = v[k >> 1];
+        const float x = __builtin_bit_cast(float, (k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        const float t = __builtin_amdgcn_fmed3f(x * r, -127.0f, 127.0f);
+        const float m = t + kMagic;
+        const float d = fabsf(t - (m - kMagic)) - 0.5f;
+        f = fminf(f, __builtin_fmaf(fabsf(t), -0x1p-20f, fabsf(d)));
+        code[k] = __builtin_bit_cast(uint32_t, m);
+    }
+    fmin = f;
+    // byte 0 of each word -> packed: sel 0x00/0x04 pick byte 0 of the second/first operand, 0x0C gives zero
+    const uint32_t lo01 = __builtin_amdgcn_perm(code[1], code[0], 0x0C0C0400u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(code[3], code[2], 0x0C0C0400u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(code[5], code[4], 0x0C0C0400u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(code[7], code[6], 0x0C0C0400u);
+    return make_uint2(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u), __builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+}
+
+__device__ __forceinline__ uint2 quant8_exact(u32x4 v, float s)
+{
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t w = v[k >> 1];
+        const float x = __builtin_bit_cast(float, (k & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        o[k >> 2] |= (uint32_t)(quant_code_exact(x, s) & 0xFF) << (8 * (k & 3));
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+__device__ __forceinline__ uint2 quant8(u32x4 v, float s, float r, bool exact_only)
+{
+    float fmin;
+    uint2 o = quant8_fast(v, r, fmin);
+    if (exact_only || !(fmin > 0.0f)) o = quant8_exact(v, s);
+    return o;
+}
+
 // Partial-maximum slots of an activation-maximum buffer (words 1.. of the
 // QVAE_ABSMAX_WORDS words): every producer writes all of them, 0 where it
 // has nothing, and the quantize pass reduces all of them.

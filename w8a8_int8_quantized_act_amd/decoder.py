@@ -19,8 +19,9 @@ residual.2 (Cin -> Cout) and residual.6 (Cout -> Cout): 2 x 2 + 4 x 3 x 2 = 28.
 The selection rules themselves are in the library (qvae_select_layer).
 
 The runner is control flow only: every layer runs in the library's kernels,
-W8A8 (absmax, quantize, INT8 conv) or native bf16, and a W8A8 layer whose
-calls return an error status runs the native conv instead.
+W8A8 (absmax, then quantize + INT8 conv or the conv that quantizes its own
+input) or native bf16, and a W8A8 layer whose calls return an error status
+runs the native conv instead.
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ import torch
 from . import ops
 
 TOP_CHANNELS = 384
+QIN_MIN_PIXELS = 256 * 128     # one 8x16-pixel full-K tile for each of 256 CUs
 
 
 @dataclass(frozen=True)
@@ -85,8 +87,14 @@ class PlannedConv:
     they serve the native layers and the fallback of the W8A8 ones."""
 
     def __init__(self, name: str, w: torch.Tensor, bias: torch.Tensor | None, preset,
-                 top_channels: int = TOP_CHANNELS, clip_ratio: float = 1.0):
+                 top_channels: int = TOP_CHANNELS, clip_ratio: float = 1.0,
+                 quantize_in_conv: bool | None = None):
         self.name = name
+        # W8A8 layers: quantize x inside the conv (absmax pass + the input-quantizing
+        # conv) or with the quantize pass (absmax + quantize + conv).  None picks the
+        # former for frames with at least QIN_MIN_PIXELS pixels (a full-K tile for
+        # every CU), where it measured faster; the results are identical.
+        self.quantize_in_conv = quantize_in_conv
         Cout, Cin, kt, kh, kw = w.shape
         self.bias = bias
         self.clip_ratio = clip_ratio
@@ -102,9 +110,19 @@ class PlannedConv:
                 self.w8a8 = False
                 self.fallbacks += 1
 
+    def uses_quantize_in_conv(self, x: torch.Tensor) -> bool:
+        if self.quantize_in_conv is not None:
+            return self.quantize_in_conv
+        return x.numel() // x.shape[-1] >= QIN_MIN_PIXELS
+
     def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         if self.w8a8:
             try:
+                if self.uses_quantize_in_conv(x):
+                    am = ops.act_absmax(x)
+                    y, _ = ops.causalconv3d_w8a8_qin(x, am, self.wq, self.ws, self.bias,
+                                                     clip_ratio=self.clip_ratio, out=out)
+                    return y
                 _, xs, xq = ops.act_absmax_quant(x, self.clip_ratio)
                 return ops.causalconv3d_w8a8(xq, xs, self.wq, self.ws, self.bias, out=out)
             except ops.QvaeError:

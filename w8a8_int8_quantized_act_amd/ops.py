@@ -20,6 +20,7 @@ Names follow the C entry points:
   causalconv3d_bf16       -> qvae_causalconv3d_bf16
   rmsnorm_silu            -> qvae_rmsnorm_silu
   rmsnorm_silu_absmax     -> qvae_rmsnorm_silu_absmax
+  causalconv3d_w8a8_qin   -> qvae_causalconv3d_w8a8_qin
 """
 from __future__ import annotations
 
@@ -85,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.qvae_rmsnorm_silu.restype = i32
         L.qvae_rmsnorm_silu_absmax.argtypes = [P, i64, i32, P, f32, P, P, P]
         L.qvae_rmsnorm_silu_absmax.restype = i32
+        L.qvae_causalconv3d_w8a8_qin.argtypes = [P, P, P, f32, P, P, P] + [i32] * 9 + [P, P, P]
+        L.qvae_causalconv3d_w8a8_qin.restype = i32
         _lib = L
     return _lib
 
@@ -315,6 +318,37 @@ def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Ten
     _check(lib().qvae_causalconv3d_w8a8_acc32(_p(xq), _p(cache), _p(wq), N, T, H, W, Cin, Cout, kt, kh, kw,
                                               _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_acc32")
     return out
+
+
+def causalconv3d_w8a8_qin(x: torch.Tensor, absmax_bits: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor,
+                          bias: torch.Tensor | None = None, cache: torch.Tensor | None = None,
+                          clip_ratio: float = 1.0, out: torch.Tensor | None = None,
+                          x_scale: torch.Tensor | None = None, stream=None):
+    """The W8A8 conv on bf16 x [N][T][H][W][Cin]: quantizes x (and the bf16 cache)
+    itself with the scale from absmax_bits (partial maxima of x) -> (y, x_scale)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(wq, "wq", torch.int8)
+    N, T, H, W, Cin = x.shape
+    if wq.dim() != 7 or tuple(wq.shape[5:]) != (64, 16):
+        raise ValueError("wq must be the packed [Cout/32][kt][Cin/32][kh][kw][64][16] tensor")
+    Cout, kt, Cin2, kh, kw = wq.shape[0] * 32, wq.shape[1], wq.shape[2] * 32, wq.shape[3], wq.shape[4]
+    if Cin2 != Cin:
+        raise ValueError(f"Cin mismatch: x has {Cin}, wq has {Cin2}")
+    if cache is not None:
+        _dev(cache, "cache", torch.bfloat16)
+        if tuple(cache.shape) != (N, kt - 1, H, W, Cin):
+            raise ValueError(f"cache must be [N][kt-1][H][W][Cin] = {(N, kt - 1, H, W, Cin)}")
+    _dev(w_scale, "w_scale", torch.float32)
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+    if out is None:
+        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=x.device)
+    if x_scale is None:
+        x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _check(lib().qvae_causalconv3d_w8a8_qin(_p(x), _p(cache), _p(absmax_bits), float(clip_ratio), _p(wq),
+                                            _p(w_scale), _p(bias), N, T, H, W, Cin, Cout, kt, kh, kw,
+                                            _p(x_scale), _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_qin")
+    return out, x_scale
 
 
 def causalconv3d_bf16(x: torch.Tensor, wp: torch.Tensor, bias: torch.Tensor | None = None,
