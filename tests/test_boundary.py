@@ -227,3 +227,12 @@ def test_absmax_words_match_header():
     from w8a8_int8_quantized_act_amd import ops
     m = re.search(r"#define\s+QVAE_ABSMAX_WORDS\s+(\d+)", open(HEADER).read())
     assert m and int(m.group(1)) == ops.ABSMAX_WORDS
+
+
+def test_binding_checks_the_maximum_buffer():
+    # the binding rejects an activation-maximum buffer in host memory before any
+    # call reaches the library (dtype and length are checked after that)
+    import torch
+    from w8a8_int8_quantized_act_amd import ops
+    with pytest.raises(ValueError, match="device"):
+        ops._absmax_buf(torch.zeros(513, dtype=torch.int32))

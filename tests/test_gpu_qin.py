@@ -117,3 +117,10 @@ def test_qin_clip_and_zero_input(ops):
     assert torch.equal(y0.view(torch.int16), y02.view(torch.int16))
     bb = torch.from_numpy(b).to(torch.bfloat16).view(torch.int16).to(DEV)
     assert torch.equal(y0.view(torch.int16).reshape(-1, C), bb.expand(N * T * H * W, C))
+
+
+def test_binding_rejects_a_short_maximum_buffer(ops):
+    x = torch.zeros(1, 1, 4, 4, 32, dtype=torch.bfloat16, device=DEV)
+    for bad in (torch.zeros(100, dtype=torch.int32, device=DEV), torch.zeros(513, dtype=torch.float32, device=DEV)):
+        with pytest.raises(ValueError):
+            ops.act_quantize(x, bad)

@@ -110,6 +110,14 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _absmax_buf(t: torch.Tensor, name: str = "absmax_bits"):
+    """An activation-maximum buffer: int32 on the device, at least ABSMAX_WORDS words."""
+    _dev(t, name, torch.int32)
+    if t.numel() < ABSMAX_WORDS:
+        raise ValueError(f"{name} must hold {ABSMAX_WORDS} int32 words, got {t.numel()}")
+    return t
+
+
 def _dev(t: torch.Tensor, name: str, dtype=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -181,6 +189,7 @@ def act_absmax(x: torch.Tensor, absmax_bits: torch.Tensor | None = None, stream=
     _dev(_bits_view(x), "x")
     if absmax_bits is None:
         absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=x.device)
+    _absmax_buf(absmax_bits)
     _check(lib().qvae_act_absmax(_p(x), x.numel(), _p(absmax_bits), _stream(stream)), "qvae_act_absmax")
     return absmax_bits
 
@@ -193,6 +202,7 @@ def act_quantize(x: torch.Tensor, absmax_bits: torch.Tensor, clip_ratio: float =
         x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
     if xq is None:
         xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _absmax_buf(absmax_bits)
     _check(lib().qvae_act_quantize(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                    _p(xq), _stream(stream)), "qvae_act_quantize")
     return x_scale, xq
@@ -210,6 +220,7 @@ def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None,
         x_scale = torch.empty((1,), dtype=torch.float32, device=dev)
     if xq is None:
         xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    _absmax_buf(absmax_bits)
     _check(lib().qvae_act_absmax_quant(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                        _p(xq), _stream(stream)), "qvae_act_absmax_quant")
     return absmax_bits, x_scale, xq
@@ -237,6 +248,7 @@ def rmsnorm_silu(x: torch.Tensor, gamma: torch.Tensor, eps: float = 1e-6, out: t
     if with_absmax:
         if absmax_bits is None:
             absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=x.device)
+        _absmax_buf(absmax_bits)
         _check(lib().qvae_rmsnorm_silu_absmax(_p(x), npix, C, _p(gamma), float(eps), _p(out), _p(absmax_bits),
                                               _stream(stream)), "qvae_rmsnorm_silu_absmax")
         return out, absmax_bits
@@ -303,6 +315,7 @@ def causalconv3d_w8a8_absmax(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.
             raise ValueError("out shape")
     if y_absmax is None:
         y_absmax = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=xq.device)
+    _absmax_buf(y_absmax, "y_absmax")
     _check(lib().qvae_causalconv3d_w8a8_absmax(_p(xq), _p(x_scale), _p(cache), _p(wq), _p(w_scale), _p(bias),
                                                N, T, H, W, Cin, Cout, kt, kh, kw, _p(out), _p(y_absmax),
                                                _stream(stream)), "qvae_causalconv3d_w8a8_absmax")
@@ -345,6 +358,7 @@ def causalconv3d_w8a8_qin(x: torch.Tensor, absmax_bits: torch.Tensor, wq: torch.
         out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=x.device)
     if x_scale is None:
         x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _absmax_buf(absmax_bits)
     _check(lib().qvae_causalconv3d_w8a8_qin(_p(x), _p(cache), _p(absmax_bits), float(clip_ratio), _p(wq),
                                             _p(w_scale), _p(bias), N, T, H, W, Cin, Cout, kt, kh, kw,
                                             _p(x_scale), _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_qin")
