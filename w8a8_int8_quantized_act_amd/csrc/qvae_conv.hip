@@ -43,10 +43,14 @@
 // product covers all 32 k of the slice whatever order the hardware sums them
 // in.  The INT32 result: lane L holds column L % 32 and, in register r, row
 // 8*(r/4) + 4*(L/32) + r%4 -- four consecutive output channels per register
-// quad.  The epilogue rescales them and transposes each 32-pixel block
-// through LDS, so every lane stores 16 contiguous bytes of the channels-last
-// output; on request it also reduces the maximum of |y| into one partial slot
-// per workgroup (the next layer's activation maximum).
+// quad.  The 16x16x64 i8 shape (used by the large 3x3 tiles, see ConvCfg):
+// lane L supplies 16 bytes of row/column (L % 16) for k-group (L / 16), again
+// the same assignment for A and B; lane L holds column L % 16 and rows
+// 4*(L/16) + {0..3} of the INT32 result.  The epilogue rescales them and
+// transposes each 32-pixel block through LDS, so every lane stores 16
+// contiguous bytes of the channels-last output; on request it also reduces
+// the maximum of |y| into one partial slot per workgroup (the next layer's
+// activation maximum).
 //
 // The same kernel, compiled with bf16 operands, is the native-precision conv
 // of the layers a preset leaves unquantized (same section, the preset list):
@@ -64,6 +68,7 @@ namespace qvae {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -119,7 +124,9 @@ constexpr int kStoreNT = 2;
 // distinct 16-byte bank groups.
 constexpr int kHaloPitch = 48;
 
-template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_>
+// (ALLOW16 = false keeps the 32x32 tiles; the launch-side quantities, threads
+// and LDS bytes, do not depend on the tile shape)
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_, bool ALLOW16 = true>
 struct ConvCfg {
     static constexpr int NW = WCO * WPX * WK;
     static constexpr int NT = NW * 64;
@@ -130,8 +137,25 @@ struct ConvCfg {
     static constexpr int KHW = KH * KW;
     static constexpr int SPW = SPW_;                         // slices per wave per stage
     static constexpr int SL = WK * SPW;                      // slices staged per stage
-    static constexpr int KS = KHW * SPW;                     // k-steps per wave per stage
-    static constexpr int PD = (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;   // weight prefetch distance
+    // Matrix instruction shape.  The 3x3 kernels with two slices per wave and
+    // stage and the large wave tiles (3 x 4 blocks, at least 4 waves) use the
+    // 16x16 tiles with 64-deep K (16x16x64 INT8, 16x16x32 bf16: the same 16
+    // bytes per lane and operand): one k-step spans both slices of one spatial
+    // tap, and each 32x32 block of the wave tile is four 16x16 accumulator
+    // blocks.  Under the chip's power limit these sustain ~13-16 % more INT8
+    // ops per second than the 32x32x32 shape on nonzero operands (same tile,
+    // same operand bytes per op).  The other kernels keep 32x32 tiles with one
+    // slice per k-step: their smaller tiles give a one-step weight prefetch too
+    // little time, and the two-wave tiles run out of registers (as does the
+    // input-quantizing conv, whose quantizer needs registers in the K loop).
+    static constexpr bool M16 = ALLOW16 && SPW == 2 && KHW > 1 && MB * NB >= 12 && NW >= 4;
+    static constexpr int MA = M16 ? 2 * MB : MB;             // accumulator blocks along the channels
+    static constexpr int NA = M16 ? 2 * NB : NB;             // accumulator blocks along the pixels
+    static constexpr int KS = M16 ? KHW : KHW * SPW;         // k-steps per wave per stage
+    // weight prefetch distance in k-steps.  A 16x16 k-step is 48 MFMAs, so one
+    // step ahead already covers an L2 round trip, and a longer ring would cost
+    // the registers the 16x16 tiles need for their wider B double buffer.
+    static constexpr int PD = M16 ? 1 : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
     static_assert(KS % PD == 0, "ring slots must repeat per stage");
     static constexpr int HALO_STORE_STEP = (PD < KS) ? PD : KS - 1;
     static constexpr int HH = TH + KH - 1;
@@ -185,8 +209,11 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
     static_assert(!(QIN && (ACC32 || OUTMAX || BF)), "the input-quantizing conv has the plain epilogue only");
     constexpr int XB = QIN ? 2 : 1;   // bytes per input value in global memory
-    using AccV = std::conditional_t<BF, v16f, v16i>;
-    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, !QIN>;
+    constexpr bool M16 = C::M16;
+    constexpr int MA = C::MA, NA = C::NA;
+    // one accumulator block: 32x32 (16 values per lane) or 16x16 (4 per lane)
+    using AccV = std::conditional_t<M16, std::conditional_t<BF, v4f, v4i>, std::conditional_t<BF, v16f, v16i>>;
     constexpr int NT = C::NT;
     constexpr int PH = (KH - 1) / 2, PW = (KW - 1) / 2;
     constexpr int ELEM = ACC32 ? 4 : 2;                  // output bytes per value
@@ -261,19 +288,32 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // offset of a fragment is wave-uniform (a scalar operand) and the lane's
     // 16 bytes are a constant vector offset, so a load needs no address
     // arithmetic.
+    // With 16x16 tiles, lane (r, g) = (lane % 16, lane / 16) of the operand of
+    // channels 16 h .. 16 h + 15 of a 32-channel block takes the 16 bytes that
+    // lane r + 16 h + 32 (g % 2) holds in the fragment of slice g / 2 (KHW
+    // fragments further on): row r + 16 h, the same k values.  The k value
+    // behind each (lane group, byte) is the same function for A and B (the B
+    // reads below pair it the same way), so the product covers the 64 k of the
+    // two slices exactly once whatever order the instruction sums them in.
     const int cb_stride = kt * S * C::KHW * 1024;          // bytes per 32-channel block (< 2^23)
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
-    const int wlane = lane * 16;
+    const int wlane = M16 ? ((lane >> 5) * C::KHW * 1024 + ((lane & 15) + 32 * ((lane >> 4) & 1)) * 16) : lane * 16;
     auto wstage = [&](const Tile &tl, int st) -> int {
         const int it = st / nsp;
         const int p = st - it * nsp;
         return (((tl.i_lo + it) * S + p * C::SL + wk * C::SPW) * C::KHW) * 1024;
     };
-    auto load_wf = [&](int off) -> v4i {
-        return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off, 0));
+    // operand row m of the ring (32-channel block m, or 16-channel half m % 2
+    // of block m / 2) for the k-step at fragment offset off
+    auto load_wf = [&](int off, int m) -> v4i {
+        if constexpr (M16)
+            return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane + (m & 1) * 256,
+                                                                                 off + (m >> 1) * cb_stride, 0));
+        else
+            return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(wrs, wlane, off + m * cb_stride, 0));
     };
-    v4i wreg[C::PD][MB];
+    v4i wreg[C::PD][MA];
 
     // ---- prologue loads: the epilogue's factors (a few words, issued first
     // so their latency hides under the rest), the weight ring, then the first
@@ -307,7 +347,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
 #pragma unroll
     for (int e = 0; e < C::PD; ++e)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
+        for (int m = 0; m < MA; ++m) wreg[e][m] = load_wf(wcur + e * 1024, m);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- halo load descriptors (stage independent parts).  Chunk u covers
@@ -418,20 +458,30 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         }
     }
 
-    // B fragment base offsets (pixel of lane, within the stage buffer)
-    int b_q0[NB];
+    // B fragment base offsets (pixel of lane, within the stage buffer).  32x32
+    // tiles: lane (lrow, lhalf) reads 16 bytes lhalf of pixel lrow of the block.
+    // 16x16 tiles: lane (r, g) reads 16 bytes g % 2 of slice g / 2 of pixel r,
+    // the k values the weight operand's lane group g holds.
+    int b_q0[NA];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int p = (wpx * NB + nb) * 32 + lrow;
-        const int pr = p / TW, pc = p - pr * TW;
-        b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + lhalf * 16 + wk * C::SPW * C::SLICE_BYTES;
+    for (int nb = 0; nb < NA; ++nb) {
+        if constexpr (M16) {
+            const int p = (wpx * NA + nb) * 16 + (lane & 15);
+            const int pr = p / TW, pc = p - pr * TW;
+            b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + ((lane >> 4) & 1) * 16 +
+                       ((lane >> 5) + wk * C::SPW) * C::SLICE_BYTES;
+        } else {
+            const int p = (wpx * NB + nb) * 32 + lrow;
+            const int pr = p / TW, pc = p - pr * TW;
+            b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + lhalf * 16 + wk * C::SPW * C::SLICE_BYTES;
+        }
     }
 
-    AccV acc[MB][NB];
+    AccV acc[MA][NA];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = AccV{};
+        for (int nb = 0; nb < NA; ++nb) acc[mb][nb] = AccV{};
 
     store_halo(0);
     __builtin_amdgcn_sched_barrier(0);
@@ -453,12 +503,12 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         const int j = tap / KW, l = tap % KW;
         return *reinterpret_cast<const v4i *>(xs + sp * C::SLICE_BYTES + (j * C::HWD + l) * kHaloPitch + b_q0[nb]);
     };
-    auto read_b = [&](const char *xs, int e, v4i (&bv)[NB]) {
+    auto read_b = [&](const char *xs, int e, v4i (&bv)[NA]) {
         const int sp = e / C::KHW, tap = e % C::KHW;
         const int j = tap / KW, l = tap % KW;
         const char *xsl = xs + sp * C::SLICE_BYTES + (j * C::HWD + l) * kHaloPitch;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
+        for (int nb = 0; nb < NA; ++nb) bv[nb] = *reinterpret_cast<const v4i *>(xsl + b_q0[nb]);
     };
 
     // One stage on the halo in buffer buf.  MORE > 0: a next stage exists (in
@@ -478,7 +528,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             for (int k = 0; k < C::HALO_PT; ++k) load_chunk(rsn, k);
         }
         const char *xs = smem + buf * C::BUF_BYTES;
-        v4i bcur[NB], bnext[NB];
+        v4i bcur[NA], bnext[NA];
         read_b(xs, 0, bcur);
         // Each k-step issues its MB x NB MFMAs with one memory instruction
         // after each of the first few: the LDS read of the next step's B
@@ -496,30 +546,36 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             const bool wload = e + C::PD < C::KS || MORE == 2;
             const int wsrc = (e + C::PD < C::KS) ? wcur + (e + C::PD) * 1024 : wnext + (e + C::PD - C::KS) * 1024;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
+            for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    constexpr int last = MB * NB - 1;
-                    const int i = mb * NB + nb;
-                    if constexpr (BF)
+                for (int nb = 0; nb < NA; ++nb) {
+                    constexpr int last = MA * NA - 1;
+                    const int i = mb * NA + nb;
+                    if constexpr (M16 && BF)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wreg[slot][mb]),
+                                                                              __builtin_bit_cast(bf16x8_t, bcur[nb]),
+                                                                              acc[mb][nb], 0, 0, 0);
+                    else if constexpr (M16)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
+                    else if constexpr (BF)
                         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wreg[slot][mb]),
                                                                               __builtin_bit_cast(bf16x8_t, bcur[nb]),
                                                                               acc[mb][nb], 0, 0, 0);
                     else
                         acc[mb][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wreg[slot][mb], bcur[nb], acc[mb][nb], 0, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);
-                    if (i < NB && e + 1 < C::KS) bnext[i] = read_b1(xs, e + 1, i);
+                    if (i < NA && e + 1 < C::KS) bnext[i] = read_b1(xs, e + 1, i);
 #pragma unroll
-                    for (int m2 = 0; m2 < MB; ++m2) {
-                        const int at = (m2 == 0) ? (NB < last ? NB : last) : (m2 + 1) * NB - 1;
-                        if (i == at && wload) wreg[slot][m2] = load_wf(wsrc + m2 * cb_stride);
+                    for (int m2 = 0; m2 < MA; ++m2) {
+                        const int at = (m2 == 0) ? (NA < last ? NA : last) : (m2 + 1) * NA - 1;
+                        if (i == at && wload) wreg[slot][m2] = load_wf(wsrc, m2);
                     }
                     if constexpr (SPREAD && MORE > 0) {
                         // halo chunk e goes out right after weight row 0, so
                         // the wait for weight row 1 of the same step (PD steps
                         // later) covers it and its store needs no extra wait
-                        constexpr int hl = NB < last ? NB : last;
-                        constexpr int hs = NB + 1 < last ? NB + 1 : last;
+                        constexpr int hl = NA < last ? NA : last;
+                        constexpr int hs = NA + 1 < last ? NA + 1 : last;
                         if (i == hl && e < C::HALO_PT) load_chunk(rsn, e);
                         if constexpr (QIN) {
                             // the two 8-value halves of the chunk are quantized in two
@@ -545,7 +601,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             __builtin_amdgcn_sched_barrier(0);
             if (e + 1 < C::KS) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) bcur[nb] = bnext[nb];
+                for (int nb = 0; nb < NA; ++nb) bcur[nb] = bnext[nb];
             }
         }
         lds_barrier();
@@ -562,21 +618,35 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         // reads the other half's export of its own blocks into registers and adds
         // it while rescaling (INT32 sums, exact in any order; FP32 sums of the
         // bf16 conv add the same two partials whichever wave finishes).
-        constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
+        constexpr int HB = (WK > 1) ? NB / 2 : NB;           // 32-pixel blocks this wave finishes
+        // A lane's accumulators of one 32-pixel block come in UNITS pieces of 4
+        // values: 32x32 tiles, unit u = (mb, g) = (u / 4, u % 4) holds channels
+        // 32 mb + 8 g + 4 lhalf + {0..3} of pixel lrow; 16x16 tiles, unit u =
+        // (m, hf) = (u / 2, u % 2) is the lane's register quad of the 16x16
+        // block (m, 2 j + hf): channels 16 m + 4 (lane / 16) + {0..3} of pixel
+        // 16 hf + lane % 16 of the 32-pixel block j.
+        constexpr int UNITS = 4 * MB;
+        auto unit_acc = [&](auto wkc, auto jc, auto uc) -> v4i {
+            constexpr int WKC = decltype(wkc)::value, j = decltype(jc)::value, u = decltype(uc)::value;
+            if constexpr (M16) {
+                return __builtin_bit_cast(v4i, acc[u >> 1][WKC * 2 * HB + 2 * j + (u & 1)]);
+            } else {
+                const v16i x = __builtin_bit_cast(v16i, acc[u >> 2][WKC * HB + j]);
+                constexpr int g = u & 3;
+                return v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+            }
+        };
         v4i part[(WK > 1) ? MB * HB * 4 : 1];
         if constexpr (WK > 1) {
             int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
             const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
             auto xport = [&](auto wkc) {
                 constexpr int other = 1 - decltype(wkc)::value;
-                static_for<MB>([&](auto mbc) {
-                    static_for<HB>([&](auto jc) {
-                        constexpr int mb = decltype(mbc)::value, j = decltype(jc)::value;
-                        const v16i v = __builtin_bit_cast(v16i, acc[mb][other * HB + j]);
-#pragma unroll
-                        for (int g = 0; g < 4; ++g)
-                            exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
-                                make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                static_for<HB>([&](auto jc) {
+                    static_for<UNITS>([&](auto uc) {
+                        constexpr int j = decltype(jc)::value, u = decltype(uc)::value;
+                        const v4i v = unit_acc(std::integral_constant<int, other>{}, jc, uc);
+                        exp_mine[(j * UNITS + u) * 64 + lane] = make_int4(v[0], v[1], v[2], v[3]);
                     });
                 });
             };
@@ -592,9 +662,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             }
         }
 
-        // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
-        // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
-        // block.  Each 32-pixel block is rescaled (one FP32 fma with the
+        // ---- epilogue.  A lane holds four consecutive output channels of a
+        // pixel per accumulator unit (the unit map above).  Each 32-pixel
+        // block is rescaled (one FP32 fma with the
         // per-channel factor and bias, then bf16 round-to-nearest-even with the
         // packed convert), written to the wave's LDS staging rows
         // [pixel][channel], then read back row-wise so every lane stores 16
@@ -627,67 +697,71 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
         // use (small tiles keep two waves per SIMD; with the output maximum a
         // workgroup running several tiles has no registers left for them)
         constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
-        f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
+        // the first channel of unit u (relative to the wave's first channel) and
+        // the pixel row it sits in within the 32-pixel block
+        auto unit_col = [&](int u) { return M16 ? (u >> 1) * 16 + 4 * (lane >> 4) : (u >> 2) * 32 + (u & 3) * 8 + lhalf * 4; };
+        auto unit_px = [&](int u) { return M16 ? (u & 1) * 16 + (lane & 15) : lrow; };
+        // distinct factor quads: one per unit (32x32), one per 16-channel row (16x16)
+        constexpr int NF = M16 ? MA : UNITS;
+        auto unit_f = [&](int u) { return M16 ? (u >> 1) : u; };
+        f4 fm[HOIST ? NF : 1], fb[HOIST ? NF : 1];
         if constexpr (HOIST) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
-                    fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
-                    fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
-                }
+            for (int k = 0; k < NF; ++k) {
+                const int col = wco * MB * 32 + unit_col(M16 ? 2 * k : k);
+                fm[k] = *reinterpret_cast<const f4 *>(s_fac + col);
+                fb[k] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
+            }
         }
         // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
         auto finish_block = [&](auto wkc, auto jc) {
             constexpr int WKC = decltype(wkc)::value;
             constexpr int j = decltype(jc)::value;
-            // the pixel this lane holds in the MFMA layout (row lrow of the block):
-            // only outputs inside the image count towards the output maximum
-            bool px_in = false;
+            // the pixels this lane holds in the matrix layout (row lrow of the
+            // block; 16x16 tiles: rows lane % 16 and 16 + lane % 16): only
+            // outputs inside the image count towards the output maximum
+            bool px_in[M16 ? 2 : 1] = {};
             if constexpr (OUTMAX) {
-                const int pl = (wpx * NB + WKC * HB + j) * 32 + lrow;
-                const int plr = pl / TW;
-                px_in = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+#pragma unroll
+                for (int hf = 0; hf < (M16 ? 2 : 1); ++hf) {
+                    const int pl = (wpx * NB + WKC * HB + j) * 32 + unit_px(hf);
+                    const int plr = pl / TW;
+                    px_in[hf] = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+                }
             }
+            static_for<UNITS>([&](auto uc) {
+                constexpr int u = decltype(uc)::value;
+                v4i v = unit_acc(wkc, jc, uc);
+                f4 vf{};
+                if constexpr (BF) {
+                    vf = __builtin_bit_cast(f4, v);
+                    if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[j * UNITS + u]);
+                } else {
+                    if constexpr (WK > 1) v += part[j * UNITS + u];
+                }
+                char *dst = stage + unit_px(u) * EPITCH + unit_col(u) * ELEM;
+                if constexpr (ACC32) {
+                    *reinterpret_cast<v4i *>(dst) = v;
+                } else {
+                    f4 y;
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const v16i x = __builtin_bit_cast(v16i, acc[mb][WKC * HB + j]);
-                    v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-                    f4 vf{};
-                    if constexpr (BF) {
-                        vf = __builtin_bit_cast(f4, v);
-                        if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[(mb * HB + j) * 4 + g]);
-                    } else {
-                        if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                    for (int e = 0; e < 4; ++e) {
+                        const float av = BF ? vf[e] : (float)v[e];
+                        if constexpr (HOIST) {
+                            y[e] = __builtin_fmaf(av, fm[unit_f(u)][e], fb[unit_f(u)][e]);
+                        } else {
+                            const int col = wco * MB * 32 + unit_col(u) + e;
+                            y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
+                        }
                     }
-                    char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
-                    if constexpr (ACC32) {
-                        *reinterpret_cast<v4i *>(dst) = v;
-                    } else {
-                        f4 y;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float av = BF ? vf[e] : (float)v[e];
-                            if constexpr (HOIST) {
-                                y[e] = __builtin_fmaf(av, fm[mb][g][e], fb[mb][g][e]);
-                            } else {
-                                const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
-                                y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
-                            }
-                        }
-                        const uint32_t lo =
-                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
-                        const uint32_t hi =
-                            __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
-                        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-                        if constexpr (OUTMAX) {
-                            if (px_in) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
-                        }
+                    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
+                    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                    if constexpr (OUTMAX) {
+                        if (px_in[M16 ? (u & 1) : 0]) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
                     }
                 }
+            });
 #pragma unroll
             for (int k = 0; k < CHUNKS / 64; ++k) {
                 const int c = k * 64 + lane;
@@ -723,15 +797,15 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
                 cur = nxt;
                 pt = ptn;
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                for (int mb = 0; mb < MA; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = AccV{};
+                    for (int nb = 0; nb < NA; ++nb) acc[mb][nb] = AccV{};
                 if constexpr (PERSIST == 1) {
                     wcur = wstage(cur, 0);
 #pragma unroll
                     for (int e = 0; e < C::PD; ++e)
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb) wreg[e][mb] = load_wf(wcur + e * 1024 + mb * cb_stride);
+                        for (int m = 0; m < MA; ++m) wreg[e][m] = load_wf(wcur + e * 1024, m);
                 }
                 continue;
             }
