@@ -73,6 +73,22 @@ def test_rmsnorm_silu_full_level_and_large_values(ops):
         assert np.array_equal(xq.cpu().numpy(), q)
 
 
+def test_rmsnorm_silu_wide_gamma_and_near_ties(ops):
+    """Normalised values far outside the SiLU's central range (|n| up to a few
+    hundred: E(-n) overflows to infinity below n ~ -88.7, and |n| > 64 takes
+    the pass's correctly rounded division), and enough values (4 M) that
+    quotients next to a bf16 rounding boundary (about 3 in 65536) occur
+    hundreds of times; h is compared bit for bit."""
+    for npix, C, gscale, seed in [(20000, 96, 40.0, 952), (1 << 15, 128, 1.0, 953)]:
+        xb, gamma = _draw(seed, npix, C, kind="normal")
+        gamma = (gamma * gscale * np.where(np.arange(C) % 3 == 0, -1.0, 1.0)).astype(np.float32)
+        x = to_dev_bits(xb).view(npix, C)
+        h = ops.rmsnorm_silu(x, torch.from_numpy(gamma).to(DEV), 1e-6)
+        torch.cuda.synchronize()
+        ref = oracle.rmsnorm_silu(xb.reshape(npix, C), gamma, 1e-6)
+        assert np.array_equal(bf16_bits(h), ref)
+
+
 def test_residual_branch_norm_silu_quantize_conv(ops):
     """x -> RMSNorm + SiLU (with the fused maximum) -> quantize (no absmax pass)
     -> W8A8 conv, against the oracle's h, its quantizer and its conv."""

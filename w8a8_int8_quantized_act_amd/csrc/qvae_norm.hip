@@ -27,6 +27,20 @@
 // (|r'| <= ln2/2 + tiny; the truncation error r'^7/7! is below 2^-27 and E is
 // within a few units in the last place of exp).
 //
+// The quotient.  n / d (d = 1 + E) must be the correctly rounded binary32
+// quotient, but only its bf16 rounding is stored.  The pass computes
+//   c = rcp(d) (hardware reciprocal, within 1 ulp),  q0 = n * c,
+//   q = fma(-fma(d, q0, -n), c, q0)
+// which is fl(n/d + eta) with |eta| a tiny fraction of an ulp of n/d (q0 is
+// within a few ulps of n/d, and the correction multiplies that error by
+// about the reciprocal's relative error), so q is the correctly rounded
+// quotient or, when n/d lies within |eta| of a midpoint between two floats,
+// its neighbour.  A neighbour changes the bf16 result only if q's low 16 bits
+// are 0x7FFF, 0x8000 or 0x8001 (next to the bf16 round-to-even boundary).
+// A group of 8 values with such a quotient, or with |n| > 64 (where d grows
+// past the range the argument needs, up to infinity), is recomputed with the
+// correctly rounded division, so h equals bf16_rne(fl(n / d)) exactly.
+//
 // Layout of one pass.  A workgroup is 4 independent waves; a wave takes
 // chunks of P consecutive pixels (P*C*2 contiguous bytes), stages them in its
 // own LDS slice (coalesced 16-byte loads, issued one chunk ahead into
@@ -44,6 +58,7 @@ typedef int v4i_n __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4_n __attribute__((ext_vector_type(4)));
 typedef float f2_n __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2_n __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_n __attribute__((ext_vector_type(2)));
 
 constexpr int kNormThreads = 256;
 constexpr int kNormWaves = kNormThreads / 64;
@@ -69,7 +84,6 @@ __device__ __forceinline__ float exp_cw(float y)
     return __builtin_amdgcn_ldexpf(p, (int)k);
 }
 
-__device__ __forceinline__ float silu_cw(float n) { return n / (1.0f + exp_cw(-n)); }
 
 // LDS written by some lanes of a wave and read by others of the same wave
 __device__ __forceinline__ void wave_lds_sync()
@@ -100,6 +114,7 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm_silu(const uint16_t *_
     const int64_t cstride = (int64_t)gridDim.x * kNormWaves;
     const float fC = (float)C;
     const int nld = (P * G + 63) / 64;                       // 16-byte loads per lane per chunk
+    const int dq = 64 / G, dg = 64 - (64 / G) * G;          // (pixel, group) step of 64 groups
     uint32_t ymax = 0;
     // The next chunk of this wave is loaded into registers while the current
     // one is processed (its loads are waited for only when it is staged).
@@ -149,22 +164,58 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm_silu(const uint16_t *_
         }
         wave_lds_sync();
         const __amdgpu_buffer_rsrc_t rout = __builtin_amdgcn_make_buffer_rsrc(h + p0 * C, 0, bytes, 0x00020000);
+        // group u = lane + 64 i is (pixel p, 16-byte group g) = (u / G, u % G),
+        // stepped without a division per group
+        int p = lane / G, g = lane - (lane / G) * G;
         for (int u = lane; u < np * G; u += 64) {
-            const int p = u / G, g = u - p * G;
             const v4i_n v = *reinterpret_cast<const v4i_n *>(s_x + p * pitch + g * 16);
             const float r = s_r[p];
-            uint32_t o[4];
+            float nv[8], dv[8], qv[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const uint32_t w = (uint32_t)v[k];
                 const float x0 = __uint_as_float(w << 16), x1 = __uint_as_float(w & 0xFFFF0000u);
-                const float n0 = (x0 * r) * s_gamma[g * 8 + 2 * k];
-                const float n1 = (x1 * r) * s_gamma[g * 8 + 2 * k + 1];
-                o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_n{silu_cw(n0), silu_cw(n1)}, bf2_n));
+                nv[2 * k] = (x0 * r) * s_gamma[g * 8 + 2 * k];
+                nv[2 * k + 1] = (x1 * r) * s_gamma[g * 8 + 2 * k + 1];
+            }
+            float namax = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                dv[k] = 1.0f + exp_cw(-nv[k]);
+                const float c = __builtin_amdgcn_rcpf(dv[k]);
+                const float q0 = nv[k] * c;
+                // the residual n - d q0 is formed as -(d q0 - n): for n = -0 it
+                // is then -0 and q keeps n's sign (-0 + -0), as n / d does
+                qv[k] = __builtin_fmaf(-__builtin_fmaf(dv[k], q0, -nv[k]), c, q0);
+                namax = __builtin_fmaxf(namax, __builtin_fabsf(nv[k]));
+            }
+            // low 16 bits of each quotient minus 0x7FFF (mod 2^16), two per register
+            u16x2_n near = u16x2_n{0xFFFF, 0xFFFF};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u16x2_n lo = __builtin_bit_cast(
+                    u16x2_n, __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, qv[2 * k + 1]),
+                                                   __builtin_bit_cast(uint32_t, qv[2 * k]), 0x05040100u));
+                near = __builtin_elementwise_min(near, lo + u16x2_n{0x8001, 0x8001});
+            }
+            if (!(namax <= 64.0f) || near.x <= 2 || near.y <= 2) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) qv[k] = nv[k] / dv[k];
+            }
+            uint32_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                o[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_n{qv[2 * k], qv[2 * k + 1]}, bf2_n));
                 if constexpr (OUTMAX) ymax = pk_absmax(ymax, o[k]);
             }
             // non-temporal: measured 4-8 % faster for this pass than the default policy
             __builtin_amdgcn_raw_buffer_store_b128(u32x4_n{o[0], o[1], o[2], o[3]}, rout, u * 16, 0, 2);
+            p += dq;
+            g += dg;
+            if (g >= G) {
+                g -= G;
+                ++p;
+            }
         }
         wave_lds_sync();   // the next chunk overwrites this wave's slice
     }
