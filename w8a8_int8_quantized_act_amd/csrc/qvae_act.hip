@@ -34,7 +34,7 @@ namespace qvae {
 typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kAbsmaxThreads = 256;
-constexpr int kAbsmaxUnroll = 4;   // 16-byte loads in flight per lane
+constexpr int kAbsmaxUnroll = 8;   // 16-byte loads in flight per lane
 static_assert(kAbsmaxParts == QVAE_ABSMAX_WORDS - 1, "one word for the maximum, the rest partials");
 
 // Number of workgroups (= partial maxima) of the absmax pass for numel.
@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t *part /* 
     m = wave_max_u32(m);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) part[wave] = m;
-    __syncthreads();
+    lds_barrier();   // (LDS only: global loads in flight need not land first)
     uint32_t b = part[0];
     for (int k = 1; k < (int)(blockDim.x >> 6); ++k) b = max(b, part[k]);
     return b;
@@ -66,10 +66,13 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * kAbsmaxThreads;
     int64_t i = (int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x;
-    for (; i + (kAbsmaxUnroll - 1) * stride < n16; i += kAbsmaxUnroll * stride) {
+    // every pass issues all of its (in-range) loads before it uses any, the
+    // last, partial pass included: one memory round trip per pass
+    for (; i < n16; i += kAbsmaxUnroll * stride) {
         u32x4 v[kAbsmaxUnroll];
 #pragma unroll
-        for (int u = 0; u < kAbsmaxUnroll; ++u) v[u] = __builtin_nontemporal_load(&x16[i + u * stride]);
+        for (int u = 0; u < kAbsmaxUnroll; ++u)
+            v[u] = (i + u * stride < n16) ? __builtin_nontemporal_load(&x16[i + u * stride]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < kAbsmaxUnroll; ++u) {
             m = pk_absmax(m, v[u].x);
@@ -77,13 +80,6 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
             m = pk_absmax(m, v[u].z);
             m = pk_absmax(m, v[u].w);
         }
-    }
-    for (; i < n16; i += stride) {
-        u32x4 v = x16[i];
-        m = pk_absmax(m, v.x);
-        m = pk_absmax(m, v.y);
-        m = pk_absmax(m, v.z);
-        m = pk_absmax(m, v.w);
     }
     if (blockIdx.x == 0 && (int)threadIdx.x < ntail) m = pk_absmax(m, tail[threadIdx.x]);
     m = max(m & 0xFFFFu, m >> 16);
@@ -118,12 +114,34 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
                                                            uint2 *__restrict__ q8,
                                                            int8_t *__restrict__ q)
 {
-    // the tensor's maximum from all partial maxima (written by the absmax pass,
-    // or by the producing convolution's epilogue; unused slots are 0)
+    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
+    int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+    // The partial maxima (written by the absmax pass, or by the producing
+    // convolution's epilogue; unused slots are 0) are loaded first, then the
+    // first unrolled pass over x.  Every wave reduces all partials itself (no
+    // workgroup barrier, whose fence would wait for the x loads too), so the
+    // reduction waits only for the partials (loads complete in order) and x's
+    // HBM latency overlaps it (at small sizes the grid covers the tensor in
+    // this one pass).
+    static_assert(kAbsmaxParts % 64 == 0, "whole partial slots per lane");
+    const int lane = threadIdx.x & 63;
+    uint32_t pv[kAbsmaxParts / 64];
+#pragma unroll
+    for (int k = 0; k < kAbsmaxParts / 64; ++k) pv[k] = absmax[1 + lane + k * 64];
+    const int64_t i0 = i;
+    // (raw buffer loads: a group past the end reads as zero, so no lane
+    // branches and the wait for the partials can leave these in flight; the
+    // first pass's offsets are below 4 x 2048 x 256 x 16 bytes)
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(x16), 0, (int)(n16 * 16 < 0x7FFFFFF0 ? n16 * 16 : 0x7FFFFFF0), 0x00020000);
+    u32x4 v0[kQuantUnroll];
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u)
+        v0[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)((i + u * stride) * 16), 0, 2));
     uint32_t mp = 0;
-    for (int k = threadIdx.x; k < kAbsmaxParts; k += kQuantThreads) mp = max(mp, absmax[1 + k]);
-    __shared__ uint32_t part[kQuantThreads / 64];
-    const uint32_t mbits = block_max_u32(mp, part);
+#pragma unroll
+    for (int k = 0; k < kAbsmaxParts / 64; ++k) mp = max(mp, pv[k]);
+    const uint32_t mbits = wave_max_u32(mp);
     const float a = bf16_bits_to_float(mbits);
     const float s = (clip_ratio * a) / 127.0f;
     const float r = 1.0f / s;
@@ -134,19 +152,23 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
         *x_scale = s;
     }
 
-    const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
-    int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
     if (zero) {
-        for (; i < n16; i += stride) q8[i] = make_uint2(0u, 0u);
+        for (i = i0; i < n16; i += stride) q8[i] = make_uint2(0u, 0u);
     } else {
-        for (; i + (kQuantUnroll - 1) * stride < n16; i += kQuantUnroll * stride) {
+        // as in the absmax pass, every pass (the last, partial one included)
+        // issues all its loads before its first store
+#pragma unroll
+        for (int u = 0; u < kQuantUnroll; ++u)
+            if (i + u * stride < n16) store_codes(&q8[i + u * stride], quant8(v0[u], s, r, exact_only));
+        for (i += kQuantUnroll * stride; i < n16; i += kQuantUnroll * stride) {
             u32x4 v[kQuantUnroll];
 #pragma unroll
-            for (int u = 0; u < kQuantUnroll; ++u) v[u] = __builtin_nontemporal_load(&x16[i + u * stride]);
+            for (int u = 0; u < kQuantUnroll; ++u)
+                v[u] = (i + u * stride < n16) ? __builtin_nontemporal_load(&x16[i + u * stride]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int u = 0; u < kQuantUnroll; ++u) store_codes(&q8[i + u * stride], quant8(v[u], s, r, exact_only));
+            for (int u = 0; u < kQuantUnroll; ++u)
+                if (i + u * stride < n16) store_codes(&q8[i + u * stride], quant8(v[u], s, r, exact_only));
         }
-        for (; i < n16; i += stride) store_codes(&q8[i], quant8(x16[i], s, r, exact_only));
     }
     // the last numel % 8 elements, one per lane of workgroup 0
     if (blockIdx.x == 0) {
