@@ -339,6 +339,7 @@ def test_conv_several_tiles_per_workgroup(ops, shape, cache_kind):
     ((2, 384, 3, 60, 120), (3, 3, 3), None),     # several tiles per workgroup
     ((1, 192, 2, 19, 23), (1, 1, 1), None),      # 1x1x1
     ((1, 64, 1, 400, 264), (3, 3, 3), None),     # narrow tiles, three workgroups per CU: the grid is capped at 512
+    ((1, 192, 2, 250, 136), (3, 3, 3), "random"),  # 192-channel 16x16 tiles (16x16 matrix tiles), ragged edges
 ])
 def test_conv_output_absmax_feeds_the_next_quantize(ops, shape, k, cache_kind):
     """The conv that also reports the partial maxima of its output: y is the
