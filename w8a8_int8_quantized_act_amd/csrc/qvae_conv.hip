@@ -124,9 +124,9 @@ constexpr int kStoreNT = 2;
 // distinct 16-byte bank groups.
 constexpr int kHaloPitch = 48;
 
-// (ALLOW16 = false keeps the 32x32 tiles; the launch-side quantities, threads
-// and LDS bytes, do not depend on the tile shape)
-template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_, bool ALLOW16 = true>
+// (QCFG: the input-quantizing conv's configuration, see M16 and HD; the
+// launch-side quantities, threads and LDS bytes, do not depend on it)
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_, bool QCFG = false>
 struct ConvCfg {
     static constexpr int NW = WCO * WPX * WK;
     static constexpr int NT = NW * 64;
@@ -148,7 +148,7 @@ struct ConvCfg {
     // slice per k-step: their smaller tiles give a one-step weight prefetch too
     // little time, and the two-wave tiles run out of registers (as does the
     // input-quantizing conv, whose quantizer needs registers in the K loop).
-    static constexpr bool M16 = ALLOW16 && SPW == 2 && KHW > 1 && MB * NB >= 12 && NW >= 4;
+    static constexpr bool M16 = !QCFG && SPW == 2 && KHW > 1 && MB * NB >= 12 && NW >= 4;
     static constexpr int MA = M16 ? 2 * MB : MB;             // accumulator blocks along the channels
     static constexpr int NA = M16 ? 2 * NB : NB;             // accumulator blocks along the pixels
     static constexpr int KS = M16 ? KHW : KHW * SPW;         // k-steps per wave per stage
@@ -157,7 +157,8 @@ struct ConvCfg {
     // the registers the 16x16 tiles need for their wider B double buffer.
     static constexpr int PD = M16 ? 1 : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
     static_assert(KS % PD == 0, "ring slots must repeat per stage");
-    static constexpr int HALO_STORE_STEP = KS - 1;   // (unspread halo: all chunks stored in the last step)
+    // (unspread halo: all chunks stored in the last step; PD for the input-quantizing conv, see HD)
+    static constexpr int HALO_STORE_STEP = (QCFG && PD < KS) ? PD : KS - 1;
     static constexpr int HH = TH + KH - 1;
     static constexpr int HWD = TW + KW - 1;
     // one 32-channel slice of the halo; slices are 32 bytes apart modulo 128
@@ -172,8 +173,10 @@ struct ConvCfg {
     static constexpr int HALO_PT = (HALO_CHUNKS + NT - 1) / NT;
     // steps between loading a halo chunk of the next stage and storing it to
     // LDS: as many as the stage allows (the last chunk is stored in the last
-    // step), so each load has most of a stage to arrive
-    static constexpr int HD = (KS - HALO_PT > PD) ? KS - HALO_PT : PD;
+    // step), so each load has most of a stage to arrive.  The input-quantizing
+    // conv stores (and codes) each chunk PD steps after its load: its chunks
+    // take twice the registers, and holding them longer costs it spills.
+    static constexpr int HD = (!QCFG && KS - HALO_PT > PD) ? KS - HALO_PT : PD;
     static constexpr int ACC_BYTES = MB * NB * 16 * 64 * 4;  // one wave's accumulators
     // split K: each wave exports the half of its blocks its partner finishes
     static constexpr int XB = ACC_BYTES / 2;
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
     static_assert(!(QIN && (ACC32 || OUTMAX || BF)), "the input-quantizing conv has the plain epilogue only");
     constexpr int XB = QIN ? 2 : 1;   // bytes per input value in global memory
-    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, !QIN>;
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, QIN>;
     constexpr bool M16 = C::M16;
     constexpr int MA = C::MA, NA = C::NA;
     // one accumulator block: 32x32 (16 values per lane) or 16x16 (4 per lane)
