@@ -155,6 +155,58 @@ def first_calls():
     print(json.dumps(out))
 
 
+def mfma_probe():
+    """The matrix cores' sustained rate per instruction shape and operand
+    distribution (qvae_probe_mfma: nothing but matrix instructions on operands
+    held in registers, one wave per SIMD on every CU): the power-limited
+    ceiling the convolution's rate is bounded by.  Median of 5 launches of
+    ~2 ms after a warm-up; 256 and 512 workgroups."""
+    import torch
+    from w8a8_int8_quantized_act_amd import ops
+    dev = "cuda:0"
+    g = torch.Generator().manual_seed(12)
+
+    def table(kind):
+        n = 14 * 4096 * 16
+        if kind == "zero":
+            b = torch.zeros(n, dtype=torch.int8)
+        elif kind == "small":
+            b = torch.randint(-5, 6, (n,), generator=g, dtype=torch.int8)
+        elif kind == "full":
+            b = torch.randint(-127, 128, (n,), generator=g, dtype=torch.int8)
+        else:   # bf16 values uniform in [-2, 2)
+            v = (torch.rand(n // 2, generator=g) * 4 - 2).to(torch.bfloat16)
+            b = v.view(torch.int8)
+        return b.view(torch.int32).reshape(14, 4096, 4).to(dev)
+
+    out = {"probe": "matrix-core rate by instruction shape and operand values", "peaks": {
+        "int8_TOPS": 5000.0, "bf16_TFLOPS": 2500.0}, "results": {}}
+    stream = torch.cuda.current_stream()
+    cases = [("i8_32x32x32", k) for k in ("zero", "small", "full")] + \
+            [("i8_16x16x64", k) for k in ("zero", "small", "full")] + \
+            [("bf16_32x32x16", k) for k in ("zero", "bf16")] + [("bf16_16x16x32", k) for k in ("zero", "bf16")]
+    for name, kind in cases:
+        shape = ops.PROBE_SHAPES[name]
+        tab = table(kind)
+        for blocks in (256, 512):
+            target = 8e12 if shape < 2 else 4e12            # ~2 ms of work per launch
+            iters = max(1, round(target / (blocks * 4 * ops.PROBE_WORK[shape])))
+            ops.probe_mfma(shape, tab, 100, blocks)
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                ops.probe_mfma(shape, tab, iters, blocks)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ms = sorted(ts)[2]
+            rate = blocks * 4 * iters * ops.PROBE_WORK[shape] / (ms * 1e-3) / 1e12
+            out["results"][f"{name}/{kind}/{blocks}"] = {"ms": round(ms, 3), "rate_T_per_s": round(rate, 1)}
+    print(json.dumps(out))
+
+
 def operand_probe(args):
     """The workload's conv (same packed weights, scale and bias) timed on int8
     inputs and caches drawn from different value distributions: the matrix
@@ -418,6 +470,8 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--first-calls", action="store_true",
                     help="only time the first and second layer step at each resolution of the level sweeps")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="sustained matrix-core rate per instruction shape and operand distribution")
     ap.add_argument("--operand-probe", action="store_true",
                     help="only time the workload's conv on int8 inputs of different value distributions")
     ap.add_argument("--frames", type=int, default=0,
@@ -441,6 +495,9 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
         return
 
+    if args.mfma_probe:
+        mfma_probe()
+        return
     if args.operand_probe:
         operand_probe(args)
         return

@@ -311,6 +311,29 @@ int qvae_causalconv3d_w8a8_acc32(const int8_t *xq, const int8_t *cache,
                                  int Cin, int Cout, int kt, int kh, int kw,
                                  int32_t *acc, void *stream);
 
+/*
+ * Matrix-core rate probe: a measurement aid for the convolution's roofline,
+ * not part of the method.  Each lane takes 14 16-byte operands from
+ * `operands` once, then issues only matrix instructions of one shape on them
+ * (cycling through them) for `iters` rounds, with no memory traffic; the
+ * caller times the launch.  The sustained rate depends on the operand values
+ * (the chip is power-limited under dense matrix load), which is what this
+ * measures.
+ *   shape     0 = INT8 32x32x32, 1 = INT8 16x16x64, 2 = bf16 32x32x16,
+ *             3 = bf16 16x16x32 (bf16 shapes read each 16 bytes as 8 bf16)
+ *   operands  int32 [14][4096][4], 16-byte aligned: lane gid = block * 256 +
+ *             thread takes entry gid % 4096 of each row (rows 0-5 A, 6-13 B)
+ *   iters     rounds, >= 1
+ *   blocks    workgroups of 256 threads (one wave per SIMD each), 1..4096
+ *   out       int32 [blocks * 256] out: one checksum of the accumulators per
+ *             lane (keeps the work; not a documented value)
+ * Work per launch = blocks * 4 waves * iters * W, with W = 24 * 65536 INT8
+ * ops (shape 0), 32 * 32768 (1), 24 * 32768 bf16 flops (2), 32 * 16384 (3).
+ * Bad shape, null pointers, iters < 1, blocks outside 1..4096 or misaligned
+ * operands: QVAE_EINVAL.
+ */
+int qvae_probe_mfma(int shape, const int32_t *operands, int iters, int blocks, int32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,6 +166,16 @@ def test_rmsnorm_silu_rejects(L):
     assert fa(FAKE, 4, 96, FAKE, 1e-6, FAKE, None, None) == -1  # no maximum buffer
 
 
+def test_probe_rejects(L):
+    f = L.qvae_probe_mfma
+    assert f(0, None, 1, 1, FAKE, None) == -1
+    assert f(0, FAKE, 0, 1, FAKE, None) == -1
+    assert f(0, FAKE, 1, 0, FAKE, None) == -1
+    assert f(0, FAKE, 1, 4097, FAKE, None) == -1
+    assert f(4, FAKE, 1, 1, FAKE, None) == -1
+    assert f(0, FAKE_MIS, 1, 1, FAKE, None) == -1
+
+
 def test_force_fail_hook():
     # QVAE_FORCE_FAIL=1: every call returns QVAE_EFORCED before any launch
     code = (
@@ -177,8 +187,9 @@ def test_force_fail_hook():
         "     L.qvae_act_absmax_quant(F, 16, 1.0, F, F, F, None),\n"
         "     L.qvae_quantize_weights(F, 32, 32, 3, 3, 3, 1.0, F, F, None),\n"
         "     L.qvae_causalconv3d_w8a8(F, F, None, F, F, None, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
-        "     L.qvae_causalconv3d_w8a8_acc32(F, None, F, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None)]\n"
-        "sys.exit(0 if r == [-4] * 6 else 1)\n")
+        "     L.qvae_causalconv3d_w8a8_acc32(F, None, F, 1, 1, 4, 4, 32, 32, 3, 3, 3, F, None),\n"
+        "     L.qvae_probe_mfma(0, F, 1, 1, F, None)]\n"
+        "sys.exit(0 if r == [-4] * 7 else 1)\n")
     env = dict(os.environ, QVAE_FORCE_FAIL="1")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqvae.so")
-SOURCES = ["qvae_act.hip", "qvae_wquant.hip", "qvae_conv.hip", "qvae_norm.hip", "qvae_plan.cpp"]
+SOURCES = ["qvae_act.hip", "qvae_wquant.hip", "qvae_conv.hip", "qvae_norm.hip", "qvae_plan.cpp", "qvae_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.qvae_rmsnorm_silu_absmax.restype = i32
         L.qvae_causalconv3d_w8a8_qin.argtypes = [P, P, P, f32, P, P, P] + [i32] * 9 + [P, P, P]
         L.qvae_causalconv3d_w8a8_qin.restype = i32
+        L.qvae_probe_mfma.argtypes = [i32, P, i32, i32, P, P]
+        L.qvae_probe_mfma.restype = i32
         _lib = L
     return _lib
 
@@ -402,3 +404,26 @@ def layer_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, bias
     _, x_scale, xq = act_absmax_quant(x, clip_ratio, stream=stream)
     y = causalconv3d_w8a8(xq, x_scale, wq, w_scale, bias, cache, stream=stream)
     return y, x_scale, xq
+
+
+PROBE_SHAPES = {"i8_32x32x32": 0, "i8_16x16x64": 1, "bf16_32x32x16": 2, "bf16_16x16x32": 3}
+# work of one wave-round per shape (INT8 ops or bf16 flops)
+PROBE_WORK = {0: 24 * 65536, 1: 32 * 32768, 2: 24 * 32768, 3: 32 * 16384}
+
+
+def probe_mfma(shape: int, operands: torch.Tensor, iters: int, blocks: int, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Matrix-core rate probe (measurement aid): `operands` int32 [14, 4096, 4]
+    on the device; returns the per-lane checksums.  The caller times it; the
+    work is blocks * 4 * iters * PROBE_WORK[shape]."""
+    _dev(operands, "operands", torch.int32)
+    if tuple(operands.shape) != (14, 4096, 4):
+        raise ValueError("operands must be int32 [14, 4096, 4]")
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=operands.device)
+    _dev(out, "out", torch.int32)
+    if out.numel() < blocks * 256:
+        raise ValueError("out must hold blocks * 256 words")
+    _check(lib().qvae_probe_mfma(int(shape), _p(operands), int(iters), int(blocks), _p(out), _stream(stream)),
+           "qvae_probe_mfma")
+    return out
