@@ -88,6 +88,12 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_mfma(const p_v4i *__res
                         asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[m * 8 + n]) : "v"(a[m]), "v"(b[n]));
                 }
         }
+        // The compiler does not see into the assembly: give the last matrix
+        // instructions' results their latency before the accumulators are read.
+        // (Both statements name every accumulator as an operand, so no read of
+        // one can be scheduled before the wait.)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]), "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]), "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]));
+        asm volatile("" : "+a"(acc[16]), "+a"(acc[17]), "+a"(acc[18]), "+a"(acc[19]), "+a"(acc[20]), "+a"(acc[21]), "+a"(acc[22]), "+a"(acc[23]), "+a"(acc[24]), "+a"(acc[25]), "+a"(acc[26]), "+a"(acc[27]), "+a"(acc[28]), "+a"(acc[29]), "+a"(acc[30]), "+a"(acc[31]));
 #pragma unroll
         for (int k = 0; k < 32; ++k)
 #pragma unroll
