@@ -167,3 +167,63 @@ def test_residual_branches_in_hip_graph(ops):
         other = ops.rmsnorm_silu(x, gd, 0.5)                    # eager work between replays
         torch.cuda.synchronize()
         del other
+
+
+def _near_tie_gammas(C, r, seed):
+    """Per-channel gammas for a pixel of all-ones x (so n_c = fl(r * gamma_c)) whose
+    SiLU quotients fl(n / (1 + E(-n))) sit next to a bf16 rounding boundary (low 16
+    bits 0x7FFF, 0x8000 or 0x8001), found with the oracle's own binary32 SiLU."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < C:
+        # positive quotients up to 12; negative ones above SiLU's minimum (~ -0.278)
+        mag = float(rng.uniform(0.05, 12.0)) if rng.random() < 0.7 else -float(rng.uniform(0.01, 0.27))
+        t_bits = (int(np.float32(mag).view(np.uint32)) & 0xFFFF0000) | 0x8000   # a bf16 tie point
+        T = float(np.uint32(t_bits).view(np.float32))
+        n = T if T > 0 else -1.0
+        for _ in range(60):   # Newton on n / (1 + exp(-n)) = T (binary64)
+            s = 1.0 / (1.0 + np.exp(-n))
+            f, df = n * s - T, s + n * s * (1.0 - s)
+            if df == 0.0:
+                break
+            n -= f / df
+        n32 = np.float32(n)
+        found = None
+        for d in range(-4, 5):
+            cand = np.float32(np.uint32(int(n32.view(np.uint32)) + d).view(np.float32))
+            q = oracle.silu_cw(float(cand))
+            if ((int(np.float32(q).view(np.uint32)) - 0x7FFF) & 0xFFFF) <= 2:
+                found = cand
+                break
+        if found is None:
+            continue
+        g0 = np.float32(float(found) / float(r))
+        for d in range(-3, 4):
+            g = np.float32(np.uint32(int(g0.view(np.uint32)) + d).view(np.float32))
+            if np.float32(r * g) == found:
+                out.append(g)
+                break
+    return np.array(out, dtype=np.float32)
+
+
+def test_rmsnorm_silu_quotients_at_bf16_boundaries(ops):
+    """Every value of pixel 0 (x = 1 in all channels) has its SiLU quotient next
+    to a bf16 rounding boundary, where the pass's reciprocal-based quotient may
+    be one ulp off and the group must take the correctly rounded division; the
+    other pixels are ordinary data.  h is compared bit for bit."""
+    C, eps = 96, 1e-6
+    r = np.float32(1.0) / np.sqrt(np.float32(np.float32(C) / np.float32(C) + np.float32(eps)))
+    gamma = _near_tie_gammas(C, r, 77)
+    ones = np.float32(1.0).view(np.uint32) >> 16
+    xb, _ = _draw(954, 300, C)
+    xb = xb.reshape(300, C).copy()
+    xb[0, :] = ones
+    # the construction holds: each quotient of pixel 0 is in the boundary window
+    for g in gamma:
+        q = oracle.silu_cw(float(np.float32(r * g)))
+        assert ((int(np.float32(q).view(np.uint32)) - 0x7FFF) & 0xFFFF) <= 2
+    x = to_dev_bits(xb).view(300, C)
+    h = ops.rmsnorm_silu(x, torch.from_numpy(gamma).to(DEV), eps)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm_silu(xb, gamma, eps)
+    assert np.array_equal(bf16_bits(h), ref)
