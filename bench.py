@@ -119,13 +119,14 @@ def cpu_baseline(ci, cache_np, budget_s=12.0, clip=1.0):
                        f"whole layer: {t_layer:.1f} s/layer")}
 
 
-def first_calls():
+def first_calls(with_init: bool = False):
     """First-call latency at each new resolution, in one process: every layer
     of the two level sweeps (new shapes, new tile configurations) runs its
     step (absmax + quantize + conv) once from a cold start at that shape, then
     again; host wall clock around each call with a device synchronize on both
     sides.  Nothing is compiled or tuned at run time: every kernel is built
-    ahead of time for gfx950."""
+    ahead of time for gfx950.  With `with_init`, qvae_init (which loads the
+    library's GPU code) runs first and is timed on its own."""
     import numpy as np
     import torch
     from w8a8_int8_quantized_act_amd import ops
@@ -137,6 +138,10 @@ def first_calls():
     torch.cuda.synchronize()
     out = {"probe": "first call per resolution", "library_and_context_ms": round((time.perf_counter() - t0) * 1e3, 2),
            "layers": []}
+    if with_init:
+        t1 = time.perf_counter()
+        ops.init()
+        out["qvae_init_ms"] = round((time.perf_counter() - t1) * 1e3, 3)
     for key in ("sweep_1024", "sweep_840x1256"):
         for ci in wl.draw_workload(key):
             spec = ci.spec
@@ -470,6 +475,7 @@ def main():
                     help="only run a plain 256 MiB device-to-device copy (counter calibration)")
     ap.add_argument("--first-calls", action="store_true",
                     help="only time the first and second layer step at each resolution of the level sweeps")
+    ap.add_argument("--init", action="store_true", help="with --first-calls: call qvae_init first")
     ap.add_argument("--mfma-probe", action="store_true",
                     help="sustained matrix-core rate per instruction shape and operand distribution")
     ap.add_argument("--operand-probe", action="store_true",
@@ -502,7 +508,7 @@ def main():
         operand_probe(args)
         return
     if args.first_calls:
-        first_calls()
+        first_calls(with_init=args.init)
         return
     if args.decoder:
         decoder_stack(args)

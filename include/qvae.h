@@ -312,6 +312,15 @@ int qvae_causalconv3d_w8a8_acc32(const int8_t *xq, const int8_t *cache,
                                  int32_t *acc, void *stream);
 
 /*
+ * Optional set-up: loads the library's GPU code for the current device and
+ * queries the device once, so that no later call pays for it (otherwise each
+ * source file's kernels are loaded on the first launch of one of them).
+ * Launches nothing and allocates nothing; calls work the same without it.
+ * Returns QVAE_OK, or QVAE_ELAUNCH if the runtime cannot provide the code.
+ */
+int qvae_init(void);
+
+/*
  * Matrix-core rate probe: a measurement aid for the convolution's roofline,
  * not part of the method.  Each lane takes 14 16-byte operands from
  * `operands` once, then issues only matrix instructions of one shape on them

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "qvae_causalconv3d_w8a8", "qvae_causalconv3d_w8a8_absmax", "qvae_causalconv3d_w8a8_acc32",
               "qvae_select_layer", "qvae_pack_weights_bf16", "qvae_causalconv3d_bf16",
               "qvae_rmsnorm_silu", "qvae_rmsnorm_silu_absmax", "qvae_causalconv3d_w8a8_qin",
-              "qvae_strerror", "qvae_version"]:
+              "qvae_strerror", "qvae_version", "qvae_init", "qvae_probe_mfma"]:
         assert n in names
 
 

@@ -56,3 +56,14 @@ def test_probe_bf16_runs_and_zero_stays_zero(ops, shape):
     out = ops.probe_mfma(shape, z, 2, 3)
     torch.cuda.synchronize()
     assert out.numel() == 3 * 256 and int(out.abs().max()) == 0
+
+
+def test_init_loads_the_code_and_changes_nothing(ops):
+    """qvae_init (optional set-up) succeeds, may be repeated, and the calls
+    after it behave as before."""
+    ops.init()
+    ops.init()
+    z = torch.zeros((14, 4096, 4), dtype=torch.int32, device=DEV)
+    out = ops.probe_mfma(0, z, 1, 1)
+    torch.cuda.synchronize()
+    assert int(out.abs().max()) == 0

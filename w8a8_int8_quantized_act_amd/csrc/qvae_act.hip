@@ -177,6 +177,14 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
     }
 }
 
+
+int preload_act()
+{
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&k_absmax)) == hipSuccess ? QVAE_OK
+                                                                                                   : QVAE_ELAUNCH;
+}
+
 }  // namespace qvae
 
 using namespace qvae;

@@ -1010,6 +1010,15 @@ static int conv_dispatch(const ConvArgs &a, int kh, int mode, hipStream_t st)
     return launch_spatial<1, 1, 1>(a, mode, st);
 }
 
+// (the plain W8A8 instantiation of the 384-channel tile: any kernel of this
+// file makes the runtime load the file's whole code object)
+int preload_conv()
+{
+    hipFuncAttributes attr;
+    const void *f = conv_kernel<4, 1, 1, 3, 4, 8, 16, 3, 3, 2>(kModePlain, false);
+    return hipFuncGetAttributes(&attr, f) == hipSuccess ? QVAE_OK : QVAE_ELAUNCH;
+}
+
 }  // namespace qvae
 
 using namespace qvae;

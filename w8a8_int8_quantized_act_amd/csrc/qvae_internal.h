@@ -47,6 +47,15 @@ inline int device_cus()
     return cus;
 }
 
+// Load this translation unit's GPU code for the current device now instead of
+// at its first launch (each source file's kernels form a code object of its
+// own); QVAE_OK or QVAE_ELAUNCH.  Used by qvae_init.
+int preload_act();
+int preload_wquant();
+int preload_conv();
+int preload_norm();
+int preload_probe();
+
 // ---- device helpers -------------------------------------------------------
 
 // bf16 bit pattern -> float (exact widening).

@@ -282,6 +282,14 @@ static int norm_validate(const uint16_t *x, int64_t npix, int C, const float *ga
     return QVAE_OK;
 }
 
+
+int preload_norm()
+{
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&k_rmsnorm_silu<64, false>)) == hipSuccess ? QVAE_OK
+                                                                                                   : QVAE_ELAUNCH;
+}
+
 }  // namespace qvae
 
 using namespace qvae;

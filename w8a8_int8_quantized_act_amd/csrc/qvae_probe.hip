@@ -102,6 +102,14 @@ __global__ __launch_bounds__(kProbeThreads) void k_probe_mfma(const p_v4i *__res
     out[gid] = sum;
 }
 
+
+int preload_probe()
+{
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&k_probe_mfma<0>)) == hipSuccess ? QVAE_OK
+                                                                                                   : QVAE_ELAUNCH;
+}
+
 }  // namespace qvae
 
 using namespace qvae;

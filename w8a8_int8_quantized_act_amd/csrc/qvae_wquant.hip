@@ -99,6 +99,14 @@ __global__ __launch_bounds__(kWqThreads) void k_pack_weights_bf16(const uint16_t
     wp[dst] = w[e];
 }
 
+int preload_wquant()
+{
+    hipFuncAttributes attr;
+    return hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(&k_quantize_weights)) == hipSuccess
+               ? QVAE_OK
+               : QVAE_ELAUNCH;
+}
+
 }  // namespace qvae
 
 using namespace qvae;
@@ -134,7 +142,16 @@ extern "C" int qvae_quantize_weights(const float *w, int Cout, int Cin, int kt, 
     return launch_status();
 }
 
-extern "C" int qvae_version(void) { return (0 << 16) | 2; }
+extern "C" int qvae_version(void) { return (0 << 16) | 3; }
+
+extern "C" int qvae_init(void)
+{
+    (void)device_cus();
+    const int r[] = {preload_act(), preload_wquant(), preload_conv(), preload_norm(), preload_probe()};
+    for (int v : r)
+        if (v != QVAE_OK) return v;
+    return QVAE_OK;
+}
 
 extern "C" const char *qvae_strerror(int status)
 {

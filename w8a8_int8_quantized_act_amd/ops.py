@@ -90,8 +90,15 @@ def lib() -> ctypes.CDLL:
         L.qvae_causalconv3d_w8a8_qin.restype = i32
         L.qvae_probe_mfma.argtypes = [i32, P, i32, i32, P, P]
         L.qvae_probe_mfma.restype = i32
+        L.qvae_init.argtypes = []
+        L.qvae_init.restype = i32
         _lib = L
     return _lib
+
+
+def init():
+    """qvae_init: load the library's GPU code for the current device now (optional)."""
+    _check(lib().qvae_init(), "qvae_init")
 
 
 def strerror(status: int) -> str:
