@@ -531,7 +531,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // between two MFMAs; otherwise all chunks are loaded at the start and
     // stored in the last step.
     constexpr bool SPREAD = C::HALO_PT + C::PD <= C::KS;
-    auto run_stage = [&](int buf, int wnext, __amdgpu_buffer_rsrc_t rsn, auto more_c) {
+    auto run_stage = [&](int buf, int wnext, __amdgpu_buffer_rsrc_t rsn, auto more_c) __attribute__((always_inline)) {
         constexpr int MORE = decltype(more_c)::value;
         if constexpr (!SPREAD && MORE > 0) {
 #pragma unroll
@@ -622,173 +622,329 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // its buffer.
     uint32_t ymax = 0;   // packed running maximum of |y| (bf16 bits) over this lane's outputs
     auto epilogue = [&](const Tile &tl) __attribute__((always_inline)) {
-        // ---- split K: each half finishes half of the pixel blocks.  Wave wk
-        // exports to LDS the blocks the other half finishes; after the barrier it
-        // reads the other half's export of its own blocks into registers and adds
-        // it while rescaling (INT32 sums, exact in any order; FP32 sums of the
-        // bf16 conv add the same two partials whichever wave finishes).
-        constexpr int HB = (WK > 1) ? NB / 2 : NB;           // 32-pixel blocks this wave finishes
-        // A lane's accumulators of one 32-pixel block come in UNITS pieces of 4
-        // values: 32x32 tiles, unit u = (mb, g) = (u / 4, u % 4) holds channels
-        // 32 mb + 8 g + 4 lhalf + {0..3} of pixel lrow; 16x16 tiles, unit u =
-        // (m, hf) = (u / 2, u % 2) is the lane's register quad of the 16x16
-        // block (m, 2 j + hf): channels 16 m + 4 (lane / 16) + {0..3} of pixel
-        // 16 hf + lane % 16 of the 32-pixel block j.
-        constexpr int UNITS = 4 * MB;
-        auto unit_acc = [&](auto wkc, auto jc, auto uc) -> v4i {
-            constexpr int WKC = decltype(wkc)::value, j = decltype(jc)::value, u = decltype(uc)::value;
-            if constexpr (M16) {
-                return __builtin_bit_cast(v4i, acc[u >> 1][WKC * 2 * HB + 2 * j + (u & 1)]);
-            } else {
-                const v16i x = __builtin_bit_cast(v16i, acc[u >> 2][WKC * HB + j]);
-                constexpr int g = u & 3;
-                return v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
-            }
-        };
-        v4i part[(WK > 1) ? MB * HB * 4 : 1];
-        if constexpr (WK > 1) {
-            int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
-            const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
-            auto xport = [&](auto wkc) {
-                constexpr int other = 1 - decltype(wkc)::value;
-                static_for<HB>([&](auto jc) {
-                    static_for<UNITS>([&](auto uc) {
+        // 16x16 tiles: accumulators in units of register quads (below); 32x32
+        // tiles: the per-(block, register group) form, kept apart so that its
+        // register allocation is the one the 32x32 kernels were tuned with
+        if constexpr (M16) {
+            // ---- split K: each half finishes half of the pixel blocks.  Wave wk
+            // exports to LDS the blocks the other half finishes; after the barrier it
+            // reads the other half's export of its own blocks into registers and adds
+            // it while rescaling (INT32 sums, exact in any order; FP32 sums of the
+            // bf16 conv add the same two partials whichever wave finishes).
+            constexpr int HB = (WK > 1) ? NB / 2 : NB;           // 32-pixel blocks this wave finishes
+            // A lane's accumulators of one 32-pixel block come in UNITS pieces of 4
+            // values: 32x32 tiles, unit u = (mb, g) = (u / 4, u % 4) holds channels
+            // 32 mb + 8 g + 4 lhalf + {0..3} of pixel lrow; 16x16 tiles, unit u =
+            // (m, hf) = (u / 2, u % 2) is the lane's register quad of the 16x16
+            // block (m, 2 j + hf): channels 16 m + 4 (lane / 16) + {0..3} of pixel
+            // 16 hf + lane % 16 of the 32-pixel block j.
+            constexpr int UNITS = 4 * MB;
+            // (every lambda that touches the accumulators is forced inline: one left
+            // out of line takes their address, and they then live in scratch memory)
+            auto unit_acc = [&](auto wkc, auto jc, auto uc) __attribute__((always_inline)) -> v4i {
+                constexpr int WKC = decltype(wkc)::value, j = decltype(jc)::value, u = decltype(uc)::value;
+                if constexpr (M16) {
+                    return __builtin_bit_cast(v4i, acc[u >> 1][WKC * 2 * HB + 2 * j + (u & 1)]);
+                } else {
+                    const v16i x = __builtin_bit_cast(v16i, acc[u >> 2][WKC * HB + j]);
+                    constexpr int g = u & 3;
+                    return v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                }
+            };
+            v4i part[(WK > 1) ? MB * HB * 4 : 1];
+            if constexpr (WK > 1) {
+                int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
+                const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
+                // The exported block is picked by value (a select on the wave-uniform
+                // wk), not by branching on wk: the optimizer merges two branches that
+                // differ only in a constant block index into one with a variable
+                // index, and a variable index sends the accumulators to scratch memory.
+                static_for<HB>([&](auto jc) __attribute__((always_inline)) {
+                    static_for<UNITS>([&](auto uc) __attribute__((always_inline)) {
                         constexpr int j = decltype(jc)::value, u = decltype(uc)::value;
-                        const v4i v = unit_acc(std::integral_constant<int, other>{}, jc, uc);
+                        const v4i a0 = unit_acc(std::integral_constant<int, 0>{}, jc, uc);
+                        const v4i a1 = unit_acc(std::integral_constant<int, 1>{}, jc, uc);
+                        const v4i v = (wk == 0) ? a1 : a0;   // the partner's half
                         exp_mine[(j * UNITS + u) * 64 + lane] = make_int4(v[0], v[1], v[2], v[3]);
                     });
                 });
-            };
-            if (wk == 0)
-                xport(std::integral_constant<int, 0>{});
-            else
-                xport(std::integral_constant<int, 1>{});
-            lds_barrier();
-#pragma unroll
-            for (int q = 0; q < MB * HB * 4; ++q) {
-                const int4 u = exp_other[q * 64 + lane];
-                part[q] = v4i{u.x, u.y, u.z, u.w};
-            }
-        }
-
-        // ---- epilogue.  A lane holds four consecutive output channels of a
-        // pixel per accumulator unit (the unit map above).  Each 32-pixel
-        // block is rescaled (one FP32 fma with the
-        // per-channel factor and bias, then bf16 round-to-nearest-even with the
-        // packed convert), written to the wave's LDS staging rows
-        // [pixel][channel], then read back row-wise so every lane stores 16
-        // contiguous bytes and consecutive lanes continue along the channels-last
-        // output row.  The stores are raw buffer stores relative to the tile's
-        // first output: a pixel outside the image gets an offset past the
-        // buffer's size and the hardware drops it, so no lane branches.
-        constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
-        constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
-        constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
-        static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
-        static_assert(32 * EPITCH <= C::epi_wave_bytes(ELEM), "staging rows fit the wave's LDS slice");
-        static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
-        // staging: with split K the partner's export slice (this wave has read it
-        // into registers and nobody else touches it); otherwise a slice per wave
-        char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : 2 * C::BUF_BYTES + wr * C::epi_wave_bytes(ELEM));
-
-        const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
-        const size_t tile_first = ((((size_t)tl.n * a.T + tl.t) * H + tl.h0) * W + tl.w0) * (size_t)a.Cout + cw0;
-        const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
-        const size_t left = (out_total - tile_first) * ELEM;
-        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-            static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
-        const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
-        typedef float f4 __attribute__((ext_vector_type(4)));
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-        // this lane's per-channel factors and biases: read from LDS once for the
-        // large wave tiles (registers to spare after the K loop), else at each
-        // use (small tiles keep two waves per SIMD; with the output maximum a
-        // workgroup running several tiles has no registers left for them)
-        constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
-        // the first channel of unit u (relative to the wave's first channel) and
-        // the pixel row it sits in within the 32-pixel block
-        auto unit_col = [&](int u) { return M16 ? (u >> 1) * 16 + 4 * (lane >> 4) : (u >> 2) * 32 + (u & 3) * 8 + lhalf * 4; };
-        auto unit_px = [&](int u) { return M16 ? (u & 1) * 16 + (lane & 15) : lrow; };
-        // distinct factor quads: one per unit (32x32), one per 16-channel row (16x16)
-        constexpr int NF = M16 ? MA : UNITS;
-        auto unit_f = [&](int u) { return M16 ? (u >> 1) : u; };
-        f4 fm[HOIST ? NF : 1], fb[HOIST ? NF : 1];
-        if constexpr (HOIST) {
-#pragma unroll
-            for (int k = 0; k < NF; ++k) {
-                const int col = wco * MB * 32 + unit_col(M16 ? 2 * k : k);
-                fm[k] = *reinterpret_cast<const f4 *>(s_fac + col);
-                fb[k] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
-            }
-        }
-        // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
-        auto finish_block = [&](auto wkc, auto jc) {
-            constexpr int WKC = decltype(wkc)::value;
-            constexpr int j = decltype(jc)::value;
-            // the pixels this lane holds in the matrix layout (row lrow of the
-            // block; 16x16 tiles: rows lane % 16 and 16 + lane % 16): only
-            // outputs inside the image count towards the output maximum
-            bool px_in[M16 ? 2 : 1] = {};
-            if constexpr (OUTMAX) {
-#pragma unroll
-                for (int hf = 0; hf < (M16 ? 2 : 1); ++hf) {
-                    const int pl = (wpx * NB + WKC * HB + j) * 32 + unit_px(hf);
-                    const int plr = pl / TW;
-                    px_in[hf] = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+                lds_barrier();
+    #pragma unroll
+                for (int q = 0; q < MB * HB * 4; ++q) {
+                    const int4 u = exp_other[q * 64 + lane];
+                    part[q] = v4i{u.x, u.y, u.z, u.w};
                 }
             }
-            static_for<UNITS>([&](auto uc) {
-                constexpr int u = decltype(uc)::value;
-                v4i v = unit_acc(wkc, jc, uc);
-                f4 vf{};
-                if constexpr (BF) {
-                    vf = __builtin_bit_cast(f4, v);
-                    if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[j * UNITS + u]);
-                } else {
-                    if constexpr (WK > 1) v += part[j * UNITS + u];
+
+            // ---- epilogue.  A lane holds four consecutive output channels of a
+            // pixel per accumulator unit (the unit map above).  Each 32-pixel
+            // block is rescaled (one FP32 fma with the
+            // per-channel factor and bias, then bf16 round-to-nearest-even with the
+            // packed convert), written to the wave's LDS staging rows
+            // [pixel][channel], then read back row-wise so every lane stores 16
+            // contiguous bytes and consecutive lanes continue along the channels-last
+            // output row.  The stores are raw buffer stores relative to the tile's
+            // first output: a pixel outside the image gets an offset past the
+            // buffer's size and the hardware drops it, so no lane branches.
+            constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
+            constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
+            constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
+            static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
+            static_assert(32 * EPITCH <= C::epi_wave_bytes(ELEM), "staging rows fit the wave's LDS slice");
+            static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
+            // staging: with split K the partner's export slice (this wave has read it
+            // into registers and nobody else touches it); otherwise a slice per wave
+            char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : 2 * C::BUF_BYTES + wr * C::epi_wave_bytes(ELEM));
+
+            const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
+            const size_t tile_first = ((((size_t)tl.n * a.T + tl.t) * H + tl.h0) * W + tl.w0) * (size_t)a.Cout + cw0;
+            const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
+            const size_t left = (out_total - tile_first) * ELEM;
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
+            const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
+            typedef float f4 __attribute__((ext_vector_type(4)));
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            // this lane's per-channel factors and biases: read from LDS once for the
+            // large wave tiles (registers to spare after the K loop), else at each
+            // use (small tiles keep two waves per SIMD; with the output maximum a
+            // workgroup running several tiles has no registers left for them)
+            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
+            // the first channel of unit u (relative to the wave's first channel) and
+            // the pixel row it sits in within the 32-pixel block
+            auto unit_col = [&](int u) __attribute__((always_inline)) { return M16 ? (u >> 1) * 16 + 4 * (lane >> 4) : (u >> 2) * 32 + (u & 3) * 8 + lhalf * 4; };
+            auto unit_px = [&](int u) __attribute__((always_inline)) { return M16 ? (u & 1) * 16 + (lane & 15) : lrow; };
+            // distinct factor quads: one per unit (32x32), one per 16-channel row (16x16)
+            constexpr int NF = M16 ? MA : UNITS;
+            auto unit_f = [&](int u) __attribute__((always_inline)) { return M16 ? (u >> 1) : u; };
+            f4 fm[HOIST ? NF : 1], fb[HOIST ? NF : 1];
+            if constexpr (HOIST) {
+    #pragma unroll
+                for (int k = 0; k < NF; ++k) {
+                    const int col = wco * MB * 32 + unit_col(M16 ? 2 * k : k);
+                    fm[k] = *reinterpret_cast<const f4 *>(s_fac + col);
+                    fb[k] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
                 }
-                char *dst = stage + unit_px(u) * EPITCH + unit_col(u) * ELEM;
-                if constexpr (ACC32) {
-                    *reinterpret_cast<v4i *>(dst) = v;
-                } else {
-                    f4 y;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float av = BF ? vf[e] : (float)v[e];
-                        if constexpr (HOIST) {
-                            y[e] = __builtin_fmaf(av, fm[unit_f(u)][e], fb[unit_f(u)][e]);
-                        } else {
-                            const int col = wco * MB * 32 + unit_col(u) + e;
-                            y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
+            }
+            // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
+            auto finish_block = [&](auto wkc, auto jc) __attribute__((always_inline)) {
+                constexpr int WKC = decltype(wkc)::value;
+                constexpr int j = decltype(jc)::value;
+                // the pixels this lane holds in the matrix layout (row lrow of the
+                // block; 16x16 tiles: rows lane % 16 and 16 + lane % 16): only
+                // outputs inside the image count towards the output maximum
+                bool px_in[M16 ? 2 : 1] = {};
+                if constexpr (OUTMAX) {
+    #pragma unroll
+                    for (int hf = 0; hf < (M16 ? 2 : 1); ++hf) {
+                        const int pl = (wpx * NB + WKC * HB + j) * 32 + unit_px(hf);
+                        const int plr = pl / TW;
+                        px_in[hf] = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+                    }
+                }
+                static_for<UNITS>([&](auto uc) __attribute__((always_inline)) {
+                    constexpr int u = decltype(uc)::value;
+                    v4i v = unit_acc(wkc, jc, uc);
+                    f4 vf{};
+                    if constexpr (BF) {
+                        vf = __builtin_bit_cast(f4, v);
+                        if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[j * UNITS + u]);
+                    } else {
+                        if constexpr (WK > 1) v += part[j * UNITS + u];
+                    }
+                    char *dst = stage + unit_px(u) * EPITCH + unit_col(u) * ELEM;
+                    if constexpr (ACC32) {
+                        *reinterpret_cast<v4i *>(dst) = v;
+                    } else {
+                        f4 y;
+    #pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float av = BF ? vf[e] : (float)v[e];
+                            if constexpr (HOIST) {
+                                y[e] = __builtin_fmaf(av, fm[unit_f(u)][e], fb[unit_f(u)][e]);
+                            } else {
+                                const int col = wco * MB * 32 + unit_col(u) + e;
+                                y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
+                            }
+                        }
+                        const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
+                        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
+                        *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                        if constexpr (OUTMAX) {
+                            if (px_in[M16 ? (u & 1) : 0]) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
                         }
                     }
-                    const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
-                    const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
-                    if constexpr (OUTMAX) {
-                        if (px_in[M16 ? (u & 1) : 0]) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
-                    }
+                });
+    #pragma unroll
+                for (int k = 0; k < CHUNKS / 64; ++k) {
+                    const int c = k * 64 + lane;
+                    const int px = c / (ROWB / 16);
+                    const int off = (c - px * (ROWB / 16)) * 16;
+                    const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
+                    const int p = (wpx * NB + WKC * HB + j) * 32 + px;
+                    const int pr = p / TW, pc = p - pr * TW;
+                    const bool inside = tl.h0 + pr < H && tl.w0 + pc < W;
+                    const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, kStoreNT);
                 }
-            });
-#pragma unroll
-            for (int k = 0; k < CHUNKS / 64; ++k) {
-                const int c = k * 64 + lane;
-                const int px = c / (ROWB / 16);
-                const int off = (c - px * (ROWB / 16)) * 16;
-                const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
-                const int p = (wpx * NB + WKC * HB + j) * 32 + px;
-                const int pr = p / TW, pc = p - pr * TW;
-                const bool inside = tl.h0 + pr < H && tl.w0 + pc < W;
-                const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, kStoreNT);
+            };
+            auto finish_all = [&](auto wkc) __attribute__((always_inline)) { static_for<HB>([&](auto jc) __attribute__((always_inline)) { finish_block(wkc, jc); }); };
+            if (WK > 1 && wk == 1)
+                finish_all(std::integral_constant<int, 1>{});
+            else
+                finish_all(std::integral_constant<int, 0>{});
+        } else {
+            // ---- split K: each half finishes half of the pixel blocks.  Wave wk
+            // exports to LDS the blocks the other half finishes; after the barrier it
+            // reads the other half's export of its own blocks into registers and adds
+            // it while rescaling (INT32 sums, exact in any order; FP32 sums of the
+            // bf16 conv add the same two partials whichever wave finishes).
+            constexpr int HB = (WK > 1) ? NB / 2 : NB;           // blocks this wave finishes
+            v4i part[(WK > 1) ? MB * HB * 4 : 1];
+            if constexpr (WK > 1) {
+                int4 *exp_mine = reinterpret_cast<int4 *>(smem + (wr * 2 + wk) * C::XB);
+                const int4 *exp_other = reinterpret_cast<const int4 *>(smem + (wr * 2 + (1 - wk)) * C::XB);
+                auto xport = [&](auto wkc) {
+                    constexpr int other = 1 - decltype(wkc)::value;
+                    static_for<MB>([&](auto mbc) {
+                        static_for<HB>([&](auto jc) {
+                            constexpr int mb = decltype(mbc)::value, j = decltype(jc)::value;
+                            const v16i v = __builtin_bit_cast(v16i, acc[mb][other * HB + j]);
+    #pragma unroll
+                            for (int g = 0; g < 4; ++g)
+                                exp_mine[((mb * HB + j) * 4 + g) * 64 + lane] =
+                                    make_int4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                        });
+                    });
+                };
+                if (wk == 0)
+                    xport(std::integral_constant<int, 0>{});
+                else
+                    xport(std::integral_constant<int, 1>{});
+                lds_barrier();
+    #pragma unroll
+                for (int q = 0; q < MB * HB * 4; ++q) {
+                    const int4 u = exp_other[q * 64 + lane];
+                    part[q] = v4i{u.x, u.y, u.z, u.w};
+                }
             }
-        };
-        auto finish_all = [&](auto wkc) { static_for<HB>([&](auto jc) { finish_block(wkc, jc); }); };
-        if (WK > 1 && wk == 1)
-            finish_all(std::integral_constant<int, 1>{});
-        else
-            finish_all(std::integral_constant<int, 0>{});
+
+            // ---- epilogue.  Lane (lrow, lhalf) holds pixel lrow of each 32-pixel
+            // block and output channels 8*g + 4*lhalf + {0..3} of each 32-channel
+            // block.  Each 32-pixel block is rescaled (one FP32 fma with the
+            // per-channel factor and bias, then bf16 round-to-nearest-even with the
+            // packed convert), written to the wave's LDS staging rows
+            // [pixel][channel], then read back row-wise so every lane stores 16
+            // contiguous bytes and consecutive lanes continue along the channels-last
+            // output row.  The stores are raw buffer stores relative to the tile's
+            // first output: a pixel outside the image gets an offset past the
+            // buffer's size and the hardware drops it, so no lane branches.
+            constexpr int ROWB = MB * 32 * ELEM;                 // one pixel's channels of this wave
+            constexpr int EPITCH = ROWB + 16;                    // odd multiple of 16 bytes
+            constexpr int CHUNKS = 32 * ROWB / 16;               // 16-byte pieces per block
+            static_assert(CHUNKS % 64 == 0, "whole chunks per lane");
+            static_assert(32 * EPITCH <= C::epi_wave_bytes(ELEM), "staging rows fit the wave's LDS slice");
+            static_assert(WK == 1 || 32 * EPITCH <= C::XB, "staging rows fit the partner's export slice");
+            // staging: with split K the partner's export slice (this wave has read it
+            // into registers and nobody else touches it); otherwise a slice per wave
+            char *stage = smem + (WK > 1 ? (wr * 2 + (1 - wk)) * C::XB : 2 * C::BUF_BYTES + wr * C::epi_wave_bytes(ELEM));
+
+            const int cw0 = co0 + wco * MB * 32;                 // first channel of this wave
+            const size_t tile_first = ((((size_t)tl.n * a.T + tl.t) * H + tl.h0) * W + tl.w0) * (size_t)a.Cout + cw0;
+            const size_t out_total = (size_t)a.N * a.T * H * W * (size_t)a.Cout;
+            const size_t left = (out_total - tile_first) * ELEM;
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<char *>(a.out) + tile_first * ELEM, 0, (int)(left < kOutside ? left : kOutside), 0x00020000);
+            const uint32_t row_bytes = (uint32_t)W * (uint32_t)a.Cout * ELEM;
+            typedef float f4 __attribute__((ext_vector_type(4)));
+            typedef float f2 __attribute__((ext_vector_type(2)));
+            typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+            // this lane's per-channel factors and biases: read from LDS once for the
+            // large wave tiles (registers to spare after the K loop), else at each
+            // use (small tiles keep two waves per SIMD; with the output maximum a
+            // workgroup running several tiles has no registers left for them)
+            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
+            f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
+            if constexpr (HOIST) {
+    #pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4;
+                        fm[mb][g] = *reinterpret_cast<const f4 *>(s_fac + col);
+                        fb[mb][g] = *reinterpret_cast<const f4 *>(s_fac + C::BCO + col);
+                    }
+            }
+            // block j (0 <= j < HB) of this wave's share; WKC = its K half (0 without split K)
+            auto finish_block = [&](auto wkc, auto jc) {
+                constexpr int WKC = decltype(wkc)::value;
+                constexpr int j = decltype(jc)::value;
+                // the pixel this lane holds in the MFMA layout (row lrow of the block):
+                // only outputs inside the image count towards the output maximum
+                bool px_in = false;
+                if constexpr (OUTMAX) {
+                    const int pl = (wpx * NB + WKC * HB + j) * 32 + lrow;
+                    const int plr = pl / TW;
+                    px_in = tl.h0 + plr < H && tl.w0 + (pl - plr * TW) < W;
+                }
+    #pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const v16i x = __builtin_bit_cast(v16i, acc[mb][WKC * HB + j]);
+                        v4i v = v4i{x[4 * g], x[4 * g + 1], x[4 * g + 2], x[4 * g + 3]};
+                        f4 vf{};
+                        if constexpr (BF) {
+                            vf = __builtin_bit_cast(f4, v);
+                            if constexpr (WK > 1) vf += __builtin_bit_cast(f4, part[(mb * HB + j) * 4 + g]);
+                        } else {
+                            if constexpr (WK > 1) v += part[(mb * HB + j) * 4 + g];
+                        }
+                        char *dst = stage + lrow * EPITCH + (mb * 32 + g * 8 + lhalf * 4) * ELEM;
+                        if constexpr (ACC32) {
+                            *reinterpret_cast<v4i *>(dst) = v;
+                        } else {
+                            f4 y;
+    #pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float av = BF ? vf[e] : (float)v[e];
+                                if constexpr (HOIST) {
+                                    y[e] = __builtin_fmaf(av, fm[mb][g][e], fb[mb][g][e]);
+                                } else {
+                                    const int col = wco * MB * 32 + mb * 32 + g * 8 + lhalf * 4 + e;
+                                    y[e] = __builtin_fmaf(av, s_fac[col], s_fac[C::BCO + col]);
+                                }
+                            }
+                            const uint32_t lo =
+                                __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[0], y[1]}, bf2));
+                            const uint32_t hi =
+                                __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{y[2], y[3]}, bf2));
+                            *reinterpret_cast<uint2 *>(dst) = make_uint2(lo, hi);
+                            if constexpr (OUTMAX) {
+                                if (px_in) ymax = pk_absmax(pk_absmax(ymax, lo), hi);
+                            }
+                        }
+                    }
+    #pragma unroll
+                for (int k = 0; k < CHUNKS / 64; ++k) {
+                    const int c = k * 64 + lane;
+                    const int px = c / (ROWB / 16);
+                    const int off = (c - px * (ROWB / 16)) * 16;
+                    const v4i v = *reinterpret_cast<const v4i *>(stage + px * EPITCH + off);
+                    const int p = (wpx * NB + WKC * HB + j) * 32 + px;
+                    const int pr = p / TW, pc = p - pr * TW;
+                    const bool inside = tl.h0 + pr < H && tl.w0 + pc < W;
+                    const uint32_t o = inside ? pr * row_bytes + (uint32_t)(pc * a.Cout * ELEM + off) : kOutside;
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), orsrc, (int)o, 0, kStoreNT);
+                }
+            };
+            auto finish_all = [&](auto wkc) { static_for<HB>([&](auto jc) { finish_block(wkc, jc); }); };
+            if (WK > 1 && wk == 1)
+                finish_all(std::integral_constant<int, 1>{});
+            else
+                finish_all(std::integral_constant<int, 0>{});
+        }
     };
     int gs = 0;   // stages run by this workgroup (buffer parity)
     for (;;) {
