@@ -32,7 +32,11 @@ import torch
 from . import ops
 
 TOP_CHANNELS = 384
-QIN_MIN_PIXELS = 256 * 128     # one 8x16-pixel full-K tile for each of 256 CUs
+# Frames from which the runner quantizes x inside the conv: the HBM-bound
+# 96-channel top level (at 1024 x 1024, 132 us against 56 + 89 us for the
+# quantize pass and the conv); at 256x256 and 512x512 the two-step path with
+# the 16x16-tile conv is faster (81 against 15 + 63 us, 104 against 28 + 72).
+QIN_MIN_PIXELS = 512 * 1024
 
 
 @dataclass(frozen=True)
@@ -92,8 +96,8 @@ class PlannedConv:
         self.name = name
         # W8A8 layers: quantize x inside the conv (absmax pass + the input-quantizing
         # conv) or with the quantize pass (absmax + quantize + conv).  None picks the
-        # former for frames with at least QIN_MIN_PIXELS pixels (a full-K tile for
-        # every CU), where it measured faster; the results are identical.
+        # former for frames with at least QIN_MIN_PIXELS pixels, where it measured
+        # faster; the results are identical.
         self.quantize_in_conv = quantize_in_conv
         Cout, Cin, kt, kh, kw = w.shape
         self.bias = bias
