@@ -668,6 +668,44 @@ def main():
     except Exception as exc:  # graphs are an extra figure, never the headline
         print(f"graph replay skipped: {exc}", file=sys.stderr)
 
+    # The matrix cores' power-limited ceiling for this layer (after the timed
+    # region): the rate of the instruction the conv uses on random full-range
+    # codes and on zeros (qvae_probe_mfma), weighted by the share of K that
+    # reads the zero cache.  The frac against it says how close the conv is
+    # to what the chip sustains on these operands, not only to the nominal peak.
+    ceiling = None
+    try:
+        shape16 = spec.k[1] == 3 and (spec.Cin // 32) % 2 == 0 and spec.Cout % 192 == 0
+        pshape = 1 if shape16 else 0
+        gp = torch.Generator().manual_seed(13)
+        tabs = {"data": torch.randint(-127, 128, (14 * 4096 * 16,), generator=gp, dtype=torch.int8)
+                .view(torch.int32).reshape(14, 4096, 4).to(dev)}
+        tabs["zero"] = torch.zeros_like(tabs["data"])
+        iters = max(1, round(8e12 / (256 * 4 * ops.PROBE_WORK[pshape])))
+        rates = {}
+        for nm, tab in tabs.items():
+            ops.probe_mfma(pshape, tab, 50, 256)
+            torch.cuda.synchronize()
+            pts = []
+            for _ in range(5):
+                q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                q0.record(stream)
+                ops.probe_mfma(pshape, tab, iters, 256)
+                q1.record(stream)
+                torch.cuda.synchronize()
+                pts.append(q0.elapsed_time(q1))
+            rates[nm] = 256 * 4 * iters * ops.PROBE_WORK[pshape] / (sorted(pts)[2] * 1e-3) / 1e12
+        kt_ = spec.k[0]
+        zero_taps = sum(max(0, kt_ - 1 - t) for t in range(spec.T)) if use_cache else 0
+        f_zero = zero_taps / (spec.T * kt_)
+        cap = 1.0 / ((1.0 - f_zero) / rates["data"] + f_zero / rates["zero"])
+        ceiling = {"instruction": "v_mfma_i32_16x16x64_i8" if shape16 else "v_mfma_i32_32x32x32_i8",
+                   "data_TOPS": round(rates["data"], 1), "zero_TOPS": round(rates["zero"], 1),
+                   "zero_share_of_K": round(f_zero, 4), "ceiling_TOPS": round(cap, 1),
+                   "frac_of_ceiling": round(conv_tops / cap, 4)}
+    except Exception as exc:  # an extra figure, never the headline
+        print(f"matrix-core ceiling probe skipped: {exc}", file=sys.stderr)
+
     # output sanity after the timed loop (no stale-output speedups)
     ref_y = ops.causalconv3d_w8a8(xq, xs, wq, ws, b, cache)
     torch.cuda.synchronize()
@@ -723,6 +761,7 @@ def main():
             "attainable_peak": round(min(PEAK_INT8_TOPS, cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 1),
             "frac_of_attainable": round(conv_tops / min(PEAK_INT8_TOPS,
                                                         cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 4),
+            "power_limited_ceiling": ceiling,
         },
         "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
         "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),
