@@ -300,6 +300,7 @@ def _compare_full(ops, ci, r, n_random=1500, seed=0, cache_zero=False):
     ((2, 384, 3, 60, 120), None),      # 384 ragged 8x16 tiles: workgroups run several, frames with 1..3 taps
     ((2, 384, 3, 60, 120), "random"),  # the same with a nonzero prev-frame cache (all taps valid)
     ((1, 192, 2, 250, 136), None),     # 288 ragged 16x16 tiles of 192 channels
+    ((1, 384, 1, 105, 157), "random"), # 6x16 tiles (180 of them in one round), ragged bottom row
 ])
 def test_conv_several_tiles_per_workgroup(ops, shape, cache_kind):
     """Shapes with more pixel tiles than CUs, so a workgroup runs tiles in a
@@ -340,6 +341,7 @@ def test_conv_several_tiles_per_workgroup(ops, shape, cache_kind):
     ((1, 192, 2, 19, 23), (1, 1, 1), None),      # 1x1x1
     ((1, 64, 1, 400, 264), (3, 3, 3), None),     # narrow tiles, three workgroups per CU: the grid is capped at 512
     ((1, 192, 2, 250, 136), (3, 3, 3), "random"),  # 192-channel 16x16 tiles (16x16 matrix tiles), ragged edges
+    ((1, 384, 1, 105, 157), (3, 3, 3), None),      # 6x16 pixel tiles
 ])
 def test_conv_output_absmax_feeds_the_next_quantize(ops, shape, k, cache_kind):
     """The conv that also reports the partial maxima of its output: y is the

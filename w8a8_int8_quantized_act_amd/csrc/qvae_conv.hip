@@ -138,7 +138,7 @@ struct ConvCfg {
     static constexpr int SPW = SPW_;                         // slices per wave per stage
     static constexpr int SL = WK * SPW;                      // slices staged per stage
     // Matrix instruction shape.  The 3x3 kernels with two slices per wave and
-    // stage and the large wave tiles (3 x 4 blocks, at least 4 waves) use the
+    // stage and the large wave tiles (3 x 4 or 3 x 3 blocks, at least 4 waves) use the
     // 16x16 tiles with 64-deep K (16x16x64 INT8, 16x16x32 bf16: the same 16
     // bytes per lane and operand): one k-step spans both slices of one spatial
     // tap, and each 32x32 block of the wave tile is four 16x16 accumulator
@@ -148,7 +148,7 @@ struct ConvCfg {
     // slice per k-step: their smaller tiles give a one-step weight prefetch too
     // little time, and the two-wave tiles run out of registers (as does the
     // input-quantizing conv, whose quantizer needs registers in the K loop).
-    static constexpr bool M16 = !QCFG && SPW == 2 && KHW > 1 && MB * NB >= 12 && NW >= 4;
+    static constexpr bool M16 = !QCFG && SPW == 2 && KHW > 1 && MB * NB >= 9 && NW >= 4;
     static constexpr int MA = M16 ? 2 * MB : MB;             // accumulator blocks along the channels
     static constexpr int NA = M16 ? 2 * NB : NB;             // accumulator blocks along the pixels
     static constexpr int KS = M16 ? KHW : KHW * SPW;         // k-steps per wave per stage
@@ -211,7 +211,7 @@ struct ConvCfg {
 // reduced from x's partial maxima in the prologue.
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW, bool ACC32, bool OUTMAX,
           bool BF, bool QIN>
-__global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 1) void k_conv_igemm(ConvArgs a)
+__global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1) void k_conv_igemm(ConvArgs a)
 {
     static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
     static_assert(!(QIN && (ACC32 || OUTMAX || BF)), "the input-quantizing conv has the plain epilogue only");
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
     // tile's first halo and, for the large wave tiles, its weight ring too (2).
     // The small tiles (1) reload the ring after the epilogue instead: holding
     // it across the epilogue would cost them their second workgroup per CU.
-    constexpr int PERSIST = WK > 1 ? 0 : (MB * NB >= 12 ? 2 : 1);
+    constexpr int PERSIST = WK > 1 ? 0 : (MB * NB >= 9 ? 2 : 1);
     __shared__ __attribute__((aligned(16))) char smem[C::lds_bytes(ELEM)];
 
     const int tid = threadIdx.x;
@@ -710,7 +710,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             // large wave tiles (registers to spare after the K loop), else at each
             // use (small tiles keep two waves per SIMD; with the output maximum a
             // workgroup running several tiles has no registers left for them)
-            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
+            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 9));
             // the first channel of unit u (relative to the wave's first channel) and
             // the pixel row it sits in within the 32-pixel block
             auto unit_col = [&](int u) __attribute__((always_inline)) { return M16 ? (u >> 1) * 16 + 4 * (lane >> 4) : (u >> 2) * 32 + (u & 3) * 8 + lhalf * 4; };
@@ -864,7 +864,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 12) ? 2 : 
             // large wave tiles (registers to spare after the K loop), else at each
             // use (small tiles keep two waves per SIMD; with the output maximum a
             // workgroup running several tiles has no registers left for them)
-            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 12));
+            constexpr bool HOIST = !ACC32 && (WK > 1 || (!OUTMAX && MB * NB >= 9));
             f4 fm[HOIST ? MB : 1][4], fb[HOIST ? MB : 1][4];
             if constexpr (HOIST) {
     #pragma unroll
@@ -1082,6 +1082,9 @@ static int64_t px_tiles(const ConvArgs &a, int th, int tw)
 // workgroup, but only while the split-K workgroups fit in one round of
 // resident workgroups (a second round would pay the fixed prologue and
 // epilogue again, and the full-K tiles then finish in one round anyway).
+// For 384 channels with full K, 6x16-pixel tiles (3 x 3 blocks per wave)
+// replace the 8x16 ones when fewer rounds of smaller tiles finish sooner
+// (384 @105x157: 140 tiles of 8x16 leave 116 CUs idle, 180 of 6x16 fewer).
 // 1x1 kernels stage two slices per wave per stage when the slice count allows
 // it, so a stage still holds more than one k-step.
 template <int KH, int KW, int SPW>
@@ -1096,8 +1099,19 @@ static int launch_spatial(const ConvArgs &a, int mode, hipStream_t st)
             const int64_t full = px_tiles(a, 8, 16) * (a.Cout / 384);
             const int64_t split = px_tiles(a, 8, 16) * (a.Cout / 192);
             if (full >= cus || !k2 ||
-                split > cus * resident_per_cu<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax))
+                split > cus * resident_per_cu<2, 1, 2, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax)) {
+                if constexpr (KH * KW > 1) {
+                    // 6x16 tiles (96 x 96 per wave) when they finish sooner: rounds of
+                    // resident workgroups times the tile's pixels, the smaller tile
+                    // taken as 8 % less efficient per pixel (less operand reuse)
+                    const int64_t t6 = px_tiles(a, 6, 16) * (a.Cout / 384);
+                    const int64_t s8 = cus * resident_per_cu<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(mode, outmax);
+                    const int64_t s6 = cus * resident_per_cu<4, 1, 1, 3, 3, 6, 16, KH, KW, SPW>(mode, outmax);
+                    const int64_t r8 = (full + s8 - 1) / s8, r6 = (t6 + s6 - 1) / s6;
+                    if (r6 * 96 * 108 < r8 * 128 * 100) return launch_cfg<4, 1, 1, 3, 3, 6, 16, KH, KW, SPW>(a, mode, st);
+                }
                 return launch_cfg<4, 1, 1, 3, 4, 8, 16, KH, KW, SPW>(a, mode, st);
+            }
         }
         if (a.Cout % 192 == 0) {
             const int64_t full = px_tiles(a, 16, 16) * (a.Cout / 192);
