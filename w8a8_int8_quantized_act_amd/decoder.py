@@ -83,6 +83,9 @@ def plan(preset, layers, top_channels: int = TOP_CHANNELS):
     return {L.name: ops.select_layer(preset, L.name, L.Cin, L.Cout, L.k, top_channels) for L in layers}
 
 
+_code_loaded = False
+
+
 class PlannedConv:
     """One decoder Conv3d run as the preset says, with per-layer fallback.
 
@@ -99,6 +102,14 @@ class PlannedConv:
         # former for frames with at least QIN_MIN_PIXELS pixels, where it measured
         # faster; the results are identical.
         self.quantize_in_conv = quantize_in_conv
+        global _code_loaded
+        if not _code_loaded:
+            # the library's GPU code is loaded at set-up, not in the first decoder step
+            try:
+                ops.init()
+            except ops.QvaeError:
+                pass   # the calls below report the failure (or fall back)
+            _code_loaded = True
         Cout, Cin, kt, kh, kw = w.shape
         self.bias = bias
         self.clip_ratio = clip_ratio
