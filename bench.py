@@ -160,6 +160,16 @@ def first_calls(with_init: bool = False):
     print(json.dumps(out))
 
 
+def zero_share_of_k(T: int, kt: int, zero_cache: bool) -> float:
+    """Share of a layer's contraction (summed over its T frames) that reads an
+    all-zero cache: frame t takes max(0, kt-1-t) of its kt temporal taps from
+    the cache.  Without a cache those taps are front padding and skipped, so
+    they are not part of K at all."""
+    if not zero_cache:
+        return 0.0
+    return sum(max(0, kt - 1 - t) for t in range(T)) / (T * kt)
+
+
 def mfma_probe():
     """The matrix cores' sustained rate per instruction shape and operand
     distribution (qvae_probe_mfma: nothing but matrix instructions on operands
@@ -695,9 +705,7 @@ def main():
                 torch.cuda.synchronize()
                 pts.append(q0.elapsed_time(q1))
             rates[nm] = 256 * 4 * iters * ops.PROBE_WORK[pshape] / (sorted(pts)[2] * 1e-3) / 1e12
-        kt_ = spec.k[0]
-        zero_taps = sum(max(0, kt_ - 1 - t) for t in range(spec.T)) if use_cache else 0
-        f_zero = zero_taps / (spec.T * kt_)
+        f_zero = zero_share_of_k(spec.T, spec.k[0], use_cache)
         cap = 1.0 / ((1.0 - f_zero) / rates["data"] + f_zero / rates["zero"])
         ceiling = {"instruction": "v_mfma_i32_16x16x64_i8" if shape16 else "v_mfma_i32_32x32x32_i8",
                    "data_TOPS": round(rates["data"], 1), "zero_TOPS": round(rates["zero"], 1),

@@ -57,3 +57,11 @@ def test_workload_op_counts_in_gop():
     for key, gops in expect.items():
         got = [round(bench.layer_counts(s, s.zero_cache)["ops"] / 1e9, 2) for s in wl.WORKLOADS[key].convs]
         assert got == gops, key
+
+
+def test_zero_share_of_k():
+    import bench
+    assert bench.zero_share_of_k(1, 3, True) == 2 / 3          # latent layer: two cache taps of three
+    assert bench.zero_share_of_k(4, 3, True) == 3 / 12         # frames 0 and 1 read 2 and 1 cache taps
+    assert bench.zero_share_of_k(8, 3, False) == 0.0           # no cache: padding taps are skipped
+    assert bench.zero_share_of_k(1, 1, True) == 0.0            # a 1x1x1 conv has no temporal taps to pad
