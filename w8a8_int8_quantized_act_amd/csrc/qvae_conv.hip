@@ -152,10 +152,13 @@ struct ConvCfg {
     static constexpr int MA = M16 ? 2 * MB : MB;             // accumulator blocks along the channels
     static constexpr int NA = M16 ? 2 * NB : NB;             // accumulator blocks along the pixels
     static constexpr int KS = M16 ? KHW : KHW * SPW;         // k-steps per wave per stage
-    // weight prefetch distance in k-steps.  A 16x16 k-step is 48 MFMAs, so one
-    // step ahead already covers an L2 round trip, and a longer ring would cost
-    // the registers the 16x16 tiles need for their wider B double buffer.
-    static constexpr int PD = M16 ? 1 : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
+    // weight prefetch distance in k-steps.  A 16x16 k-step is 48 MFMAs, enough
+    // for an L2 hit but not for a weight row that the pass before the conv
+    // pushed out of L2.  The split-K 16x16 tile (two waves per K half) has the
+    // registers for a three-step ring (all 512, none spilled) and takes it:
+    // 4-5 % off its launch after the quantize pass.  The single-K 16x16 tiles
+    // spill with three slots and keep one.
+    static constexpr int PD = M16 ? (WK > 1 ? 3 : 1) : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
     static_assert(KS % PD == 0, "ring slots must repeat per stage");
     // (unspread halo: all chunks stored in the last step; PD for the input-quantizing conv, see HD)
     static constexpr int HALO_STORE_STEP = (QCFG && PD < KS) ? PD : KS - 1;
