@@ -124,9 +124,11 @@ constexpr int kStoreNT = 2;
 // distinct 16-byte bank groups.
 constexpr int kHaloPitch = 48;
 
-// (QCFG: the input-quantizing conv's configuration, see M16 and HD; the
-// launch-side quantities, threads and LDS bytes, do not depend on it)
-template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_, bool QCFG = false>
+// (QCFG: the input-quantizing conv's configuration, see M16 and HD; ACC32_:
+// the INT32-output conv's, see PD; the launch-side quantities, threads and
+// LDS bytes, depend on neither)
+template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW_, bool QCFG = false,
+          bool ACC32_ = false>
 struct ConvCfg {
     static constexpr int NW = WCO * WPX * WK;
     static constexpr int NT = NW * 64;
@@ -154,11 +156,12 @@ struct ConvCfg {
     static constexpr int KS = M16 ? KHW : KHW * SPW;         // k-steps per wave per stage
     // weight prefetch distance in k-steps.  A 16x16 k-step is 48 MFMAs, enough
     // for an L2 hit but not for a weight row that the pass before the conv
-    // pushed out of L2.  The split-K 16x16 tile (two waves per K half) has the
-    // registers for a three-step ring (all 512, none spilled) and takes it:
-    // 4-5 % off its launch after the quantize pass.  The single-K 16x16 tiles
-    // spill with three slots and keep one.
-    static constexpr int PD = M16 ? (WK > 1 ? 3 : 1) : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
+    // pushed out of L2.  The 16x16 tiles with the registers for a three-step
+    // ring take it (4-5 % off their launches, none spilled): the split-K tile
+    // and the 96 x 96 wave tile, the latter not in its INT32-output form.  The
+    // 96 x 128 single-K tile spills with three slots and keeps one.
+    static constexpr int PD = M16 ? ((WK > 1 || (NB == 3 && !ACC32_)) ? 3 : 1)
+                                  : (KS % 3 == 0) ? 3 : (KS % 2 == 0) ? 2 : 1;
     static_assert(KS % PD == 0, "ring slots must repeat per stage");
     // (unspread halo: all chunks stored in the last step; PD for the input-quantizing conv, see HD)
     static constexpr int HALO_STORE_STEP = (QCFG && PD < KS) ? PD : KS - 1;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
     static_assert(!(BF && (ACC32 || OUTMAX)), "the bf16 conv has the plain epilogue only");
     static_assert(!(QIN && (ACC32 || OUTMAX || BF)), "the input-quantizing conv has the plain epilogue only");
     constexpr int XB = QIN ? 2 : 1;   // bytes per input value in global memory
-    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, QIN>;
+    using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW, QIN, ACC32>;
     constexpr bool M16 = C::M16;
     constexpr int MA = C::MA, NA = C::NA;
     // one accumulator block: 32x32 (16 values per lane) or 16x16 (4 per lane)
