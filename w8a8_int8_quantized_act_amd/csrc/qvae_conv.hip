@@ -357,11 +357,6 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
     __builtin_amdgcn_sched_barrier(0);
 
     int wcur = wstage(cur, 0);
-#pragma unroll
-    for (int e = 0; e < C::PD; ++e)
-#pragma unroll
-        for (int m = 0; m < MA; ++m) wreg[e][m] = load_wf(wcur + e * 1024, m);
-    __builtin_amdgcn_sched_barrier(0);
 
     // ---- halo load descriptors (stage independent parts).  Chunk u covers
     // pixel q = u / (2*SL) and 16 bytes c = u % (2*SL) of its SL slices, so
@@ -447,6 +442,14 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
 
     set_hoff(cur);
     load_halo(cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the weight ring after the first halo: loads complete in issue order, so
+    // the halo's LDS stores and the barrier before the first stage wait for
+    // the halo alone and the ring's rows stay in flight until their MFMAs
+#pragma unroll
+    for (int e = 0; e < C::PD; ++e)
+#pragma unroll
+        for (int m = 0; m < MA; ++m) wreg[e][m] = load_wf(wcur + e * 1024, m);
     __builtin_amdgcn_sched_barrier(0);
 
     // QIN: the tensor maximum from the partial maxima (while the first halo is
