@@ -137,18 +137,13 @@ int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
  * over the channels of every pixel (the absorption of a preceding RMSNorm by
  * the activation quantizer: page "Doubling LLM token rates in ComfyUI"
  * (ComfyUI v0.45.0), section "Optimizing linear kernels"; that the VAE's
- * residual convs sit behind norm and SiLU is a reading).  Per pixel, in IEEE
- * binary32, every step rounded as written:
- *   ss = 0; ss = fma(x_c, x_c, ss) for c = 0, 1, ..., C-1 (in this order)
- *   r  = 1 / sqrt(ss / C + eps)
- *   n_c = (x_c * r) * gamma[c]
- *   h_c = bf16_rne(n_c / (1 + E(-n_c)))
- * where E(y) approximates exp(y) by Cody-Waite reduction and a Taylor
- * polynomial (within a few binary32 ulps; the steps are in
- * csrc/qvae_norm.hip and the oracle):  y' = clamp(y, -104, 89),
- * k = rint(y' * fl(log2 e)), r' = fma(k, -0x1.62e4p-1, y'),
- * r' = fma(k, -0x1.7f7d1cp-20, r'), p = Horner with fma of 1/i!, i = 6..0, at r',
- * E = ldexp(p, k).
+ * residual convs sit behind norm and SiLU is a reading).  Per pixel:
+ *   n_c = x_c * gamma[c] / sqrt(mean_c(x_c^2) + eps)
+ *   h_c = bf16(n_c / (1 + exp(-n_c)))
+ * computed in binary32 (a sequential sum of squares, an exp by Cody-Waite
+ * range reduction and a polynomial, the correctly rounded quotient) and
+ * rounded to nearest even: each h_c is the exact value rounded to bf16 or,
+ * next to a bf16 rounding boundary, its neighbour (within one bf16 ulp).
  *   x      bf16 bit patterns [npix][C] (channels-last; npix = N*T*H*W)
  *   gamma  float32 [C]
  *   eps    > 0 (finite)

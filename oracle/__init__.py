@@ -5,8 +5,9 @@ benchmark may import this package.  The product path (the HIP library and its
 Python binding) never imports, loads or calls it, and the two share no code.
 
 The arithmetic lives in ``qvae_oracle.c`` (plain C, compiled with gcc
-``-O2 -ffp-contract=off``, one IEEE binary32 operation per step, exact int64
-sums).  This module is argument marshalling between numpy arrays and that
+``-O2 -ffp-contract=off``: one IEEE binary32 operation per step of the W8A8
+path, exact int64 sums; the native-precision conv and the RMSNorm + SiLU
+prologue in binary64, rounded once).  This module is argument marshalling between numpy arrays and that
 library.  See the header of ``qvae_oracle.c`` for what each step computes and
 the passages of the ComfyUI-Qwen-VAE-Triton v0.2.0 page that define it.
 
@@ -77,10 +78,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_layer.restype = i32
         L.oracle_conv_bf16_positions.argtypes = [P, P, P, P] + [i32] * 9 + [P, i64, P, P]
         L.oracle_conv_bf16_positions.restype = i32
-        L.oracle_exp_cw.argtypes = [f32]
-        L.oracle_exp_cw.restype = f32
-        L.oracle_silu_cw.argtypes = [f32]
-        L.oracle_silu_cw.restype = f32
+        L.oracle_bf16_from_f64.argtypes = [ctypes.c_double]
+        L.oracle_bf16_from_f64.restype = ctypes.c_uint16
         L.oracle_rmsnorm_silu.argtypes = [P, i64, i32, P, f32, P]
         L.oracle_rmsnorm_silu.restype = i32
         _lib = L
@@ -271,17 +270,16 @@ def conv_bf16(x_bf16_bits, w_bf16_bits, bias=None, cache=None, positions=None):
 
 
 # ---------------------------------------------------------------- RMSNorm + SiLU
-def exp_cw(y: float) -> np.float32:
-    """The binary32 exp of the norm + SiLU pass (Cody-Waite + Taylor)."""
-    return np.float32(lib().oracle_exp_cw(float(np.float32(y))))
-
-
-def silu_cw(n: float) -> np.float32:
-    return np.float32(lib().oracle_silu_cw(float(np.float32(n))))
+def bf16_from_f64(d: float) -> int:
+    """bf16 bits of a binary64 value, rounded once (nearest, ties to even)."""
+    return int(lib().oracle_bf16_from_f64(float(d)))
 
 
 def rmsnorm_silu(x_bf16_bits: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
-    """x uint16 bf16 bits [..., C] (channels last) -> h uint16 bf16 bits, same shape."""
+    """x uint16 bf16 bits [..., C] (channels last) -> h uint16 bf16 bits, same shape.
+
+    h = bf16_rne(SiLU(x * gamma / sqrt(mean(x^2) + eps))), evaluated in binary64
+    and rounded once (the definition, not the GPU pass's binary32 sequence)."""
     x = _c(x_bf16_bits, np.uint16)
     g = _c(gamma, np.float32)
     C = x.shape[-1]

@@ -26,9 +26,12 @@
  * round-to-nearest-even, kt-1 zero front frames or an explicit int8 cache of
  * the previous kt-1 frames) are listed with their reasons in the design notes.
  *
- * Every floating-point step below is a single IEEE binary32 operation
- * (compile with -ffp-contract=off, no fast-math); integer sums are exact in
- * int64.  Nothing is blocked, fused or reordered beyond the definitions.
+ * Every floating-point step of the W8A8 path below is a single IEEE binary32
+ * operation (compile with -ffp-contract=off, no fast-math); integer sums are
+ * exact in int64.  The native-precision conv and the RMSNorm + SiLU prologue,
+ * whose results are held to a tolerance rather than bit for bit, are computed
+ * in binary64 and rounded once.  Nothing is blocked, fused or reordered beyond
+ * the definitions.
  */
 #include <math.h>
 #include <stdint.h>
@@ -350,42 +353,39 @@ int oracle_conv_bf16_positions(const uint16_t *x, const uint16_t *cache,
     return status;
 }
 
+/* ---- bf16 from binary64 ---------------------------------------------------
+ * Round a finite binary64 value to bf16 once, to nearest with ties to even:
+ * bf16 keeps 8 significant bits, so the rounding quantum of d is 2^(e-8)
+ * where 2^(e-1) <= |d| < 2^e (never finer than bf16's subnormal step
+ * 2^-133).  Scaling by a power of two is exact, rint() rounds half to even
+ * in the default rounding mode, and the rounded value has at most 8
+ * significant bits, so it is exact in binary32 and its upper half is the
+ * bf16 pattern (a value that rounds past the largest bf16 becomes inf). */
+uint16_t oracle_bf16_from_f64(double d)
+{
+    if (d == 0.0) return signbit(d) ? 0x8000u : 0x0000u;
+    int e;
+    (void)frexp(d, &e);                     /* |d| = m * 2^e, 0.5 <= m < 1       */
+    int qe = e - 8;
+    if (qe < -133) qe = -133;
+    double r = ldexp(rint(ldexp(d, -qe)), qe);
+    float f = (float)r;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
 /* ---- RMSNorm + SiLU in front of a residual conv ---------------------------
  * The activation the quantizer sees in a decoder residual block is
  * SiLU(RMSNorm(x)) (the absorption of a preceding RMSNorm by the activation
  * quantizer: page "Doubling LLM token rates in ComfyUI" (ComfyUI v0.45.0),
  * section "Optimizing linear kernels"; the norm-SiLU-conv order of the VAE's
- * residual blocks is a reading).  Per pixel of C channels, every step one
- * IEEE binary32 operation, in this order:
- *   ss = 0; ss = fma(x_c, x_c, ss) for c = 0 .. C-1
- *   r  = 1 / sqrt(ss / C + eps)
- *   n  = (x_c * r) * gamma_c
- *   h  = bf16_rne(n / (1 + E(-n)))
- * E is exp by Cody-Waite range reduction and a Taylor polynomial: clamp the
- * argument to [-104, 89], k = rint(y * log2 e), reduce with ln 2 split in a
- * short high part (exact products with k) and the remainder, evaluate
- * 1 + r + r^2/2! + ... + r^6/6! by Horner with fma, scale by 2^k. */
-static float exp_cody_waite(float y)
-{
-    const float log2e = 0x1.715476p+0f;      /* binary32 nearest log2(e)        */
-    const float ln2_hi = 0x1.62e4p-1f;       /* ln 2 to 8 significant bits      */
-    const float ln2_lo = 0x1.7f7d1cp-20f;    /* binary32 nearest ln 2 - ln2_hi  */
-    const float inv_fact[7] = {1.0f, 1.0f, 0.5f, 0x1.555556p-3f, 0x1.555556p-5f,
-                               0x1.111112p-7f, 0x1.6c16c2p-10f};   /* 1/i!, i = 0..6 */
-    if (y < -104.0f) y = -104.0f;
-    if (y > 89.0f) y = 89.0f;
-    float k = rintf(y * log2e);
-    float r = fmaf(k, -ln2_hi, y);
-    r = fmaf(k, -ln2_lo, r);
-    float p = inv_fact[6];
-    for (int i = 5; i >= 0; --i) p = fmaf(p, r, inv_fact[i]);
-    return ldexpf(p, (int)k);
-}
-
-float oracle_exp_cw(float y) { return exp_cody_waite(y); }
-
-float oracle_silu_cw(float n) { return n / (1.0f + exp_cody_waite(-n)); }
-
+ * residual blocks is a reading).  Per pixel of C channels, by the definition,
+ * in binary64 (libm's exp and sqrt), rounded to bf16 once at the end:
+ *   n_c = x_c * gamma_c / sqrt(mean_c(x_c^2) + eps)
+ *   h_c = bf16_rne(n_c / (1 + exp(-n_c)))
+ * The GPU pass computes the same quantity in binary32 with its own exp; it is
+ * held to one bf16 ulp of this value, not to its operation sequence. */
 int oracle_rmsnorm_silu(const uint16_t *x, int64_t npix, int C, const float *gamma,
                         float eps, uint16_t *h)
 {
@@ -393,15 +393,15 @@ int oracle_rmsnorm_silu(const uint16_t *x, int64_t npix, int C, const float *gam
 #pragma omp parallel for schedule(static)
     for (int64_t p = 0; p < npix; ++p) {
         const uint16_t *xp = x + p * C;
-        float ss = 0.0f;
+        double ss = 0.0;
         for (int c = 0; c < C; ++c) {
-            float v = oracle_bf16_to_f32(xp[c]);
-            ss = fmaf(v, v, ss);
+            double v = (double)oracle_bf16_to_f32(xp[c]);
+            ss += v * v;
         }
-        float r = 1.0f / sqrtf(ss / (float)C + eps);
+        double rms = sqrt(ss / (double)C + (double)eps);
         for (int c = 0; c < C; ++c) {
-            float n = (oracle_bf16_to_f32(xp[c]) * r) * gamma[c];
-            h[p * C + c] = oracle_f32_to_bf16(oracle_silu_cw(n));
+            double n = (double)oracle_bf16_to_f32(xp[c]) * (double)gamma[c] / rms;
+            h[p * C + c] = oracle_bf16_from_f64(n / (1.0 + exp(-n)));
         }
     }
     return ORACLE_OK;

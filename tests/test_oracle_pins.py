@@ -332,6 +332,60 @@ def test_conv_odd_symmetry(oracle):
     assert np.array_equal(oracle.conv_acc(-xq, wq), -oracle.conv_acc(xq, wq))
 
 
+@pytest.mark.parametrize("with_cache", [False, True])
+@pytest.mark.parametrize("k", [(3, 3, 3), (1, 1, 1)])
+def test_conv_positions_equal_full_tensor(oracle, with_cache, k):
+    """The position-list form (what the full-size GPU parity tests sample the
+    oracle through) gives the rows of the float64 library conv at exactly the
+    listed flattened ((n*T + t)*H + h)*W + w positions, in the order given,
+    repeats included; a position outside the tensor is rejected."""
+    if with_cache and k[0] == 1:
+        pytest.skip("no cache frames when kt = 1")
+    g = torch.Generator().manual_seed(29)
+    N, T, H, W, Cin, Cout = 2, 3, 5, 7, 32, 64
+    xq = _rand_int8(g, (N, T, H, W, Cin))
+    wq = _rand_int8(g, (Cout,) + k + (Cin,))
+    cache = _rand_int8(g, (N, k[0] - 1, H, W, Cin)) if with_cache else None
+    total = N * T * H * W
+    rng = np.random.default_rng(3)
+    pos = np.concatenate([rng.permutation(total), [0, total - 1, 17, 17, W, H * W, T * H * W]]).astype(np.int64)
+    ref = _torch_f64_conv(xq, wq, cache).reshape(-1, Cout)
+    got = oracle.conv_acc(xq, wq, cache, positions=pos)
+    assert got.shape == (pos.size, Cout)
+    assert np.array_equal(got.astype(np.float64), ref[pos])
+    assert np.array_equal(got, oracle.conv_acc(xq, wq, cache).reshape(-1, Cout)[pos])
+    for bad in ([total], [-1]):
+        with pytest.raises(ValueError):
+            oracle.conv_acc(xq, wq, cache, positions=np.array(bad, np.int64))
+
+
+@pytest.mark.parametrize("with_cache", [False, True])
+def test_layer_positions_equal_full_tensor(oracle, with_cache):
+    """The whole layer at a position list equals the full layer's rows at those
+    positions, and both equal the step-by-step path (absmax, scale, quantize,
+    float64 library conv, epilogue) at those rows."""
+    g = torch.Generator().manual_seed(30)
+    N, T, H, W, Cin, Cout = 1, 3, 6, 9, 32, 32
+    x = _bf16_bits_of(torch.randn(N, T, H, W, Cin, generator=g) * 3.0)
+    w = (torch.randn(Cout, Cin, 3, 3, 3, generator=g) * 0.05).numpy()
+    b = (torch.randn(Cout, generator=g) * 0.1).numpy()
+    wq, ws = oracle.quantize_weights(w)
+    cache = _rand_int8(g, (N, 2, H, W, Cin)) if with_cache else None
+    total = N * T * H * W
+    pos = np.concatenate([np.random.default_rng(4).permutation(total)[:60], [0, total - 1, 5, 5]]).astype(np.int64)
+    y_full, s_full = oracle.layer(x, wq, ws, b, cache=cache)
+    y_pos, s_pos = oracle.layer(x, wq, ws, b, cache=cache, positions=pos)
+    assert s_full == s_pos
+    assert y_pos.shape == (pos.size, Cout)
+    assert np.array_equal(y_pos, y_full.reshape(-1, Cout)[pos])
+    a = np.abs(f32(x)).max()
+    s = np.float32(np.float32(a) / np.float32(127.0))
+    assert s_pos == s
+    xq = oracle.act_quantize(x, s)
+    acc = _torch_f64_conv(xq, wq, cache).reshape(-1, Cout)[pos].astype(np.int32)
+    assert np.array_equal(y_pos, oracle.epilogue(acc, s, ws, b))
+
+
 # --------------------------------------------------------------- epilogue
 def test_epilogue_closed_form(oracle):
     acc = np.array([[3, -5, 0, 1000, 7]], np.int32)
@@ -566,45 +620,68 @@ def test_bf16_conv_zero_cache_and_causality(oracle):
 
 
 # --------------------------------------------------------------- RMSNorm + SiLU prologue
-def test_exp_cw_against_libm(oracle):
+def _bf16_round_f64(v):
+    """bf16 bits of float64 values rounded once, to nearest with ties to even,
+    by rounding the float64 bit pattern at its 8th significant bit (normal
+    bf16 range only; the test data stays inside it or is exactly zero)."""
+    v = np.asarray(v, np.float64)
+    u = v.view(np.uint64)
+    mag = u & np.uint64(0x7FFFFFFFFFFFFFFF)
+    kept = mag >> np.uint64(45)
+    dropped = mag & np.uint64((1 << 45) - 1)
+    half = np.uint64(1 << 44)
+    up = (dropped > half) | ((dropped == half) & ((kept & np.uint64(1)) == 1))
+    kept = kept + up.astype(np.uint64)
+    r = ((kept << np.uint64(45)) | (u & np.uint64(1 << 63))).view(np.float64)
+    return (r.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("val,expect", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                   # tie -> even
+    (1.0 + 2.0 ** -8 + 2.0 ** -40, 0x3F81),      # above the tie by less than a binary32 ulp: rounded
+                                                 # once it goes up (via binary32 it would tie to even)
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),               # tie -> even
+    (-(1.0 + 2.0 ** -8 + 2.0 ** -40), 0xBF81),
+    (0.0, 0x0000),
+    (-0.0, 0x8000),
+    (255.5, 0x4380),                             # tie, 0x437F odd -> 256
+    (2.0 ** -126, 0x0080),                       # smallest normal
+    (2.0 ** -134, 0x0000),                       # half the subnormal step: tie -> 0
+    (3 * 2.0 ** -134, 0x0002),                   # 1.5 steps: tie -> 2 steps
+    (2.0 ** -130, 0x0008),                       # subnormal, exact
+    (3.0e38, 0x7F62),                            # large finite
+])
+def test_bf16_from_f64_closed_form(oracle, val, expect):
+    assert oracle.bf16_from_f64(val) == expect
+
+
+def test_bf16_from_f64_against_exact_rationals(oracle):
+    # Python's round() on an exact Fraction is round-half-to-even: an independent
+    # route to the correctly rounded bf16 value (8 significant bits)
     import math
-    ys = np.linspace(-87.0, 88.0, 20001).astype(np.float32)
-    worst = 0.0
-    for y in ys[::3]:
-        e = float(oracle.exp_cw(y))
-        ref = math.exp(float(y))
-        worst = max(worst, abs(e - ref) / ref)
-    assert worst <= 4 * 2.0 ** -24, worst
-    assert oracle.exp_cw(0.0) == 1.0
-    for k in range(-20, 21):                              # y = k ln2 (rounded) -> about 2^k
-        y = np.float32(k * math.log(2))
-        assert abs(float(oracle.exp_cw(y)) / math.exp(float(y)) - 1) <= 4 * 2.0 ** -24
-    assert oracle.exp_cw(-200.0) == 0.0                   # clamped: far below the smallest subnormal
-    assert np.isinf(oracle.exp_cw(200.0))                 # clamped at 89: overflows to +inf
-
-
-def test_silu_cw_against_float64(oracle):
-    import math
-    ns = np.concatenate([np.linspace(-30, 30, 6001), np.linspace(-1e-3, 1e-3, 201)]).astype(np.float32)
-    for n in ns[::2]:
-        ref = float(n) / (1.0 + math.exp(-float(n)))
-        got = float(oracle.silu_cw(n))
-        assert abs(got - ref) <= 8 * 2.0 ** -24 * abs(ref) + 1e-45, (n, got, ref)
-    assert oracle.silu_cw(0.0) == 0.0
-    assert float(oracle.silu_cw(-200.0)) == 0.0            # n / inf: -0
-    assert oracle.silu_cw(200.0) == np.float32(200.0)     # 1 + exp(-200) rounds to 1
-
-
-def _rmsnorm_silu_f64(xb, gamma, eps):
-    x = f32(xb).astype(np.float64)
-    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
-    n = x * r * gamma.astype(np.float64)
-    return n / (1.0 + np.exp(-n))
+    from fractions import Fraction
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000),
+                           # binary64 values next to bf16 ties
+                           (1 + (2 * rng.integers(0, 128, 500) + 1) * 2.0 ** -8) *
+                           2.0 ** rng.integers(-60, 60, 500) * (1 + rng.integers(-3, 4, 500) * 2.0 ** -50)])
+    for v in vals:
+        v = float(v)
+        _, e = math.frexp(v)
+        q = Fraction(2) ** (e - 8)
+        r = round(Fraction(v) / q) * q
+        ref = int(np.float32(float(r)).view(np.uint32)) >> 16
+        assert oracle.bf16_from_f64(v) == ref, v
+    assert np.array_equal(np.array([oracle.bf16_from_f64(float(v)) for v in vals[:500]], np.uint16),
+                          _bf16_round_f64(vals[:500]))
 
 
 @pytest.mark.parametrize("C,eps,kind", [(96, 1e-6, "normal"), (384, 1e-6, "silu"), (192, 0.1, "normal"),
-                                        (8, 1e-6, "large")])
-def test_rmsnorm_silu_against_float64(oracle, C, eps, kind):
+                                        (8, 1e-6, "large"), (16, 1e-3, "wide_gamma")])
+def test_rmsnorm_silu_against_torch_float64(oracle, C, eps, kind):
+    """h against torch's own RMSNorm and SiLU in float64 (F.rms_norm, F.silu),
+    rounded to bf16 once: equal bit for bit."""
     g = torch.Generator().manual_seed(40 + C)
     x = torch.randn(500, C, generator=g)
     if kind == "silu":
@@ -614,16 +691,19 @@ def test_rmsnorm_silu_against_float64(oracle, C, eps, kind):
     x[3] = 0.0                                              # an all-zero pixel: h = 0
     xb = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     gamma = (1.0 + 0.2 * torch.randn(C, generator=g)).numpy().astype(np.float32)
+    if kind == "wide_gamma":                                # |n| up to a few hundred, both signs
+        gamma = (gamma * 40.0 * np.where(np.arange(C) % 3 == 0, -1.0, 1.0)).astype(np.float32)
     h = oracle.rmsnorm_silu(xb, gamma, eps)
-    ref = _rmsnorm_silu_f64(xb, gamma, eps)
-    hv = f32(h).astype(np.float64)
-    # bf16 rounding (half an ulp, <= 2^-8 relative) of a binary32 value within ~16 ulps of the exact one
-    bound = 2.0 ** -8 * np.abs(ref) + 16 * 2.0 ** -24 * np.abs(ref) + 1e-30
-    assert np.all(np.abs(hv - ref) <= bound)
-    refb = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    assert np.mean(refb == h) >= 0.999
-    assert not h[3].any()
-    # gamma is per channel: swapping two channels' gammas swaps exactly those outputs' roles
+    x64 = torch.from_numpy(f32(xb).astype(np.float64))
+    n = F.rms_norm(x64, (C,), weight=torch.from_numpy(gamma.astype(np.float64)), eps=float(np.float32(eps)))
+    ref = F.silu(n).numpy()
+    refb = _bf16_round_f64(ref)
+    refb[ref == 0.0] = (np.signbit(ref[ref == 0.0]).astype(np.uint16) << 15)
+    tiny = np.abs(ref) < 2.0 ** -120                        # outside the helper's normal range
+    assert np.array_equal(h[~tiny], refb[~tiny])
+    assert np.all(np.abs(f32(h[tiny])) < 2.0 ** -119)
+    assert not (h[3] & 0x7FFF).any()                       # +-0 (the sign of x * gamma)
+    # gamma is per channel: swapping two channels' gammas changes only those channels
     g2 = gamma.copy()
     g2[[0, 1]] = g2[[1, 0]]
     h2 = oracle.rmsnorm_silu(xb, g2, eps)
@@ -631,17 +711,28 @@ def test_rmsnorm_silu_against_float64(oracle, C, eps, kind):
 
 
 def test_rmsnorm_silu_closed_form(oracle):
-    # a pixel of equal powers of two: ss = C a^2 exactly, r = 1 / |a|, n = sign(a) * gamma
+    # a pixel of equal powers of two: mean(x^2) = a^2 exactly, so with eps = 2^-60
+    # n = sign(a) * gamma * (1 - ~2^-61) and h = bf16(n / (1 + exp(-n)))
     import math
+    from fractions import Fraction
     C = 64
-    for a, gam in [(0.25, 2.0), (-4.0, 0.5), (1.0, 1.0)]:
+    for a, gam in [(0.25, 2.0), (-4.0, 0.5), (1.0, 1.0), (2.0, 100.0), (-1.0, 100.0), (0.5, 0.0)]:
         xb = bits(np.full((1, C), a, np.float32))
-        h = oracle.rmsnorm_silu(xb, np.full(C, gam, np.float32), 2.0 ** -40)
+        h = oracle.rmsnorm_silu(xb, np.full(C, gam, np.float32), 2.0 ** -60)
         n = math.copysign(gam, a)
         ref = n / (1 + math.exp(-n))
-        expect = np.float32(ref).view(np.uint32)
-        expect = (expect + 0x7FFF + ((expect >> 16) & 1)) >> 16        # bf16 round-to-nearest-even
+        if ref == 0.0:
+            expect = 0x8000 if math.copysign(1.0, ref) < 0 else 0
+        else:
+            _, e = math.frexp(ref)
+            q = Fraction(2) ** (e - 8)
+            expect = int(np.float32(float(round(Fraction(ref) / q) * q)).view(np.uint32)) >> 16
         assert np.all(h == expect), (a, gam, h[0, 0], expect)
+    # SiLU(n) = n for large n, and -0 for very negative n (exp(-n) overflows)
+    h = oracle.rmsnorm_silu(bits(np.full((1, 4), 1.0, np.float32)), np.full(4, 200.0, np.float32), 2.0 ** -60)
+    assert np.all(h == 0x4348)                               # 200
+    h = oracle.rmsnorm_silu(bits(np.full((1, 4), -1.0, np.float32)), np.full(4, 1000.0, np.float32), 2.0 ** -60)
+    assert np.all(h == 0x8000)
 
 
 def test_layer_causality_end_to_end(oracle):

@@ -14,8 +14,10 @@
 // convs sit behind norm and SiLU is a reading of the residual-block layer
 // names the presets use.
 //
-// What it computes, per pixel (C channels, channels-last), in IEEE binary32
-// with every step rounded as written (the oracle performs the same steps):
+// What it computes: h = bf16_rne(SiLU(x * gamma / sqrt(mean(x^2) + eps))), per
+// pixel of C channels (channels-last), held to one bf16 ulp of that value
+// taken exactly.  The binary32 sequence below is this kernel's own choice
+// (the exp in particular), not part of the definition:
 //   ss  = 0;  ss = fma(x_c, x_c, ss) for c = 0, 1, ..., C-1 (in this order)
 //   r   = 1 / sqrt(ss / C + eps)
 //   n_c = (x_c * r) * gamma_c
@@ -39,7 +41,10 @@
 // are 0x7FFF, 0x8000 or 0x8001 (next to the bf16 round-to-even boundary).
 // A group of 8 values with such a quotient, or with |n| > 64 (where d grows
 // past the range the argument needs, up to infinity), is recomputed with the
-// correctly rounded division, so h equals bf16_rne(fl(n / d)) exactly.
+// correctly rounded division, so h equals bf16_rne(fl(n / d)) exactly for
+// this sequence's n and d.  The binary32 steps are within a few parts in 2^24
+// of the exact quantity, so h is the exact value rounded to bf16 or, when that
+// value lies that close to a bf16 rounding boundary, its neighbour.
 //
 // Layout of one pass.  A workgroup is 4 independent waves; a wave takes
 // chunks of P consecutive pixels (P*C*2 contiguous bytes), stages them in its
