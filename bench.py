@@ -1,20 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the W8A8 INT8 CausalConv3d hot path on one MI355X.
 
-A step is one pass of the whole per-layer path over one batch of synthetic
-input that is already resident in HBM:
-    absmax (HBM pass) -> quantize (HBM pass) -> implicit-GEMM conv with fused
-    FP32 rescale + bias + bf16 store.
-Weight quantization happens once at load, outside the timed region.
-
-Default workload: the latent-level layer, Cin=Cout=384, 3x3x3, input
-[1,384,1,128,128] bf16 with 5 % x20 outliers and an explicit 2-frame zero
-cache (all 27 taps are data).  ``--workload`` picks another layer.
+Default workload: the video-style chunked causal decode, input
+[1,384,8,90,160] bf16 ~N(0,1).  One step, with every input resident in HBM:
+    absmax + quantize over all 8 frames (one scale for every chunk),
+    4 chunk convs 3x3x3 384->384 of 2 frames each (chunk 0 with causal front
+    padding, chunks 1-3 with the previous chunk's 2 int8 frames as cache),
+    the 1x1x1 384->192 projection over the same int8 input,
+each conv with its fused FP32 rescale + bias + bf16 store.  Weight
+quantization happens once at load, outside the timed region.
+``--workload`` picks a single layer instead (absmax + quantize + conv).
 
 Prints ONE JSON line.  ``value`` is INT8 TOPS of the whole step (algorithmic
 conv ops / step time); the ``roofline`` object covers the dominant kernel
-(the conv), timed with HIP events around every launch on the stream it runs
-on; ``cpu_baseline`` is the CPU oracle on a bounded sample of the same layer.
+(the 3x3x3 conv: the four chunk launches), timed with HIP events around its
+launches on the stream it runs on; ``cpu_baseline`` is the CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -168,116 +169,6 @@ def zero_share_of_k(T: int, kt: int, zero_cache: bool) -> float:
     if not zero_cache:
         return 0.0
     return sum(max(0, kt - 1 - t) for t in range(T)) / (T * kt)
-
-
-def mfma_probe():
-    """The matrix cores' sustained rate per instruction shape and operand
-    distribution (qvae_probe_mfma: nothing but matrix instructions on operands
-    held in registers, one wave per SIMD on every CU): the power-limited
-    ceiling the convolution's rate is bounded by.  Median of 5 launches of
-    ~2 ms after a warm-up; 256 and 512 workgroups."""
-    import torch
-    from w8a8_int8_quantized_act_amd import ops
-    dev = "cuda:0"
-    g = torch.Generator().manual_seed(12)
-
-    def table(kind):
-        n = 14 * 4096 * 16
-        if kind == "zero":
-            b = torch.zeros(n, dtype=torch.int8)
-        elif kind == "small":
-            b = torch.randint(-5, 6, (n,), generator=g, dtype=torch.int8)
-        elif kind == "full":
-            b = torch.randint(-127, 128, (n,), generator=g, dtype=torch.int8)
-        else:   # bf16 values uniform in [-2, 2)
-            v = (torch.rand(n // 2, generator=g) * 4 - 2).to(torch.bfloat16)
-            b = v.view(torch.int8)
-        return b.view(torch.int32).reshape(14, 4096, 4).to(dev)
-
-    out = {"probe": "matrix-core rate by instruction shape and operand values", "peaks": {
-        "int8_TOPS": 5000.0, "bf16_TFLOPS": 2500.0}, "results": {}}
-    stream = torch.cuda.current_stream()
-    cases = [("i8_32x32x32", k) for k in ("zero", "small", "full")] + \
-            [("i8_16x16x64", k) for k in ("zero", "small", "full")] + \
-            [("bf16_32x32x16", k) for k in ("zero", "bf16")] + [("bf16_16x16x32", k) for k in ("zero", "bf16")]
-    for name, kind in cases:
-        shape = ops.PROBE_SHAPES[name]
-        tab = table(kind)
-        for blocks in (256, 512):
-            target = 8e12 if shape < 2 else 4e12            # ~2 ms of work per launch
-            iters = max(1, round(target / (blocks * 4 * ops.PROBE_WORK[shape])))
-            ops.probe_mfma(shape, tab, 100, blocks)
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(5):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                ops.probe_mfma(shape, tab, iters, blocks)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            ms = sorted(ts)[2]
-            rate = blocks * 4 * iters * ops.PROBE_WORK[shape] / (ms * 1e-3) / 1e12
-            out["results"][f"{name}/{kind}/{blocks}"] = {"ms": round(ms, 3), "rate_T_per_s": round(rate, 1)}
-    print(json.dumps(out))
-
-
-def operand_probe(args):
-    """The workload's conv (same packed weights, scale and bias) timed on int8
-    inputs and caches drawn from different value distributions: the matrix
-    cores' throughput depends on the operand values (power), not only on the
-    instruction count.  Inputs are seeded draws; nothing is checked against the
-    oracle here (the kernels' parity is the tests' job)."""
-    import torch
-    from w8a8_int8_quantized_act_amd import ops
-    from w8a8_int8_quantized_act_amd import workloads as wl
-    dev = "cuda:0"
-    ci = wl.draw_workload(args.workload, only=args.level)[-1]
-    spec = ci.spec
-    kt = spec.k[0]
-    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev))
-    b = torch.from_numpy(ci.b).to(dev)
-    xs = torch.tensor([0.01], dtype=torch.float32, device=dev)
-    y = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev)
-    g = torch.Generator().manual_seed(11)
-    shape = (spec.N, spec.T, spec.H, spec.W, spec.Cin)
-    cshape = (spec.N, kt - 1, spec.H, spec.W, spec.Cin)
-
-    def codes(kind, shp):
-        if kind == "zero":
-            return torch.zeros(shp, dtype=torch.int8)
-        if kind == "small":
-            return torch.randint(-5, 6, shp, generator=g, dtype=torch.int8)
-        if kind == "silu":
-            z = torch.randn(shp, generator=g)
-            v = z * torch.sigmoid(z)
-            return torch.round(v / (v.abs().max() / 127)).clamp(-127, 127).to(torch.int8)
-        return torch.randint(-127, 128, shp, generator=g, dtype=torch.int8)
-
-    cnt = layer_counts(spec, True)
-    out = {"probe": "conv time by operand distribution", "workload": args.workload, "level": args.level,
-           "algorithmic_ops": cnt["ops"], "note": "input and 2-frame cache drawn from the same distribution; "
-           "median of 5 runs of 20 back-to-back launches (HIP events)", "results": {}}
-    stream = torch.cuda.current_stream()
-    for kind in ("zero", "small", "silu", "full"):
-        xq = codes(kind, shape).to(dev)
-        cache = codes(kind, cshape).to(dev) if kt > 1 else None
-        run = lambda: ops.causalconv3d_w8a8(xq, xs, wq, ws, b, cache, out=y)
-        for _ in range(3):
-            run()
-        torch.cuda.synchronize()
-        meds = []
-        for _ in range(5):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(20):
-                run()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            meds.append(e0.elapsed_time(e1) / 20)
-        ms = sorted(meds)[2]
-        out["results"][kind] = {"conv_us": round(ms * 1e3, 2), "tops": round(cnt["ops"] / (ms * 1e-3) / 1e12, 1)}
-    print(json.dumps(out))
 
 
 def decoder_cpu_baseline(data, budget_s=12.0):
@@ -472,84 +363,365 @@ def decoder_stack(args):
                               "K back-to-back stacks, median of 3"}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="latent_384_128_cache")
-    ap.add_argument("--level", type=int, default=0, help="layer index inside a level sweep")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
-    ap.add_argument("--first-calls", action="store_true",
-                    help="only time the first and second layer step at each resolution of the level sweeps")
-    ap.add_argument("--init", action="store_true", help="with --first-calls: call qvae_init first")
-    ap.add_argument("--mfma-probe", action="store_true",
-                    help="sustained matrix-core rate per instruction shape and operand distribution")
-    ap.add_argument("--operand-probe", action="store_true",
-                    help="only time the workload's conv on int8 inputs of different value distributions")
-    ap.add_argument("--frames", type=int, default=0,
-                    help="a multi-frame variant: the layer's shape with T frames (redrawn, same recipe)")
-    ap.add_argument("--clip", type=float, default=1.0,
-                    help="activation and weight clip ratio in (0, 1] (the page fixes 1.0)")
-    ap.add_argument("--decoder", action="store_true",
-                    help="only time the decoder's 28 residual-block convs per preset (W8A8 vs native bf16)")
-    ap.add_argument("--out-h", type=int, default=1024)
-    ap.add_argument("--out-w", type=int, default=1024)
-    args = ap.parse_args()
+def chunk_launches(spec):
+    """The convs of one chunked-decode step, in launch order, with their
+    algorithmic work: chunk c covers frames [c*F, (c+1)*F) (F = T / chunks) and
+    reads the previous F frames of the same int8 input as its cache (chunk 0:
+    causal front padding), then the 1x1x1 projection runs over all T frames."""
+    fpc = spec.T // spec.chunks
+    out = []
+    for c in range(spec.chunks):
+        cs = dataclasses.replace(spec, T=fpc, chunks=1, proj_cout=0, zero_cache=False, name=f"{spec.name}_chunk{c}")
+        out.append(dict(name=f"chunk{c}", spec=cs, frame0=c * fpc, cache_frame0=(c - 1) * fpc if c else None,
+                        **layer_counts(cs, c > 0)))
+    if spec.proj_cout:
+        ps = dataclasses.replace(spec, Cout=spec.proj_cout, k=(1, 1, 1), chunks=1, proj_cout=0, zero_cache=False,
+                                 name=f"{spec.name}_proj")
+        out.append(dict(name="proj", spec=ps, frame0=0, cache_frame0=None, **layer_counts(ps, False)))
+    return out
 
-    if args.copy_probe:
-        import torch
-        n = 256 << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+
+def _events(k):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(k)]
+
+
+def _make_timer(stream):
+    import torch
+
+    def timed(fn, k):
+        """k back-to-back calls on the stream, bracketed by synchronize and by
+        two HIP events on that stream -> (wall ms, event ms) per call."""
+        e0, e1 = _events(2)
         torch.cuda.synchronize()
-        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
-        return
+        t0 = time.perf_counter()
+        e0.record(stream)
+        rc = 0
+        for _ in range(k):
+            rc |= fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert rc == 0
+        return wall * 1e3 / k, e0.elapsed_time(e1) / k
 
-    if args.mfma_probe:
-        mfma_probe()
-        return
-    if args.operand_probe:
-        operand_probe(args)
-        return
-    if args.first_calls:
-        first_calls(with_init=args.init)
-        return
-    if args.decoder:
-        decoder_stack(args)
-        return
+    def per_launch(fns, k):
+        """Each of k rounds of the launches in fns between its own pair of
+        events -> per-launch durations in ms (one list per launch of fns)."""
+        evs = [[_events(2) for _ in fns] for _ in range(k)]
+        torch.cuda.synchronize()
+        for r in range(k):
+            for (e0, e1), fn in zip(evs[r], fns):
+                e0.record(stream)
+                assert fn() == 0
+                e1.record(stream)
+        torch.cuda.synchronize()
+        return [[evs[r][i][0].elapsed_time(evs[r][i][1]) for r in range(k)] for i in range(len(fns))]
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the W8A8 CausalConv3d path here runs on a single MI355X "
-              "(multi-GPU sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
+    def cold(fn, reps=10):
+        """One launch after a 1 GiB write on the same stream evicted the 256 MB
+        last-level cache, between two events; median of reps."""
+        import numpy as np
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+        e0, e1 = _events(2)
+        ts = []
+        for i in range(reps):
+            scratch.fill_(i & 0xFF)
+            e0.record(stream)
+            assert fn() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        del scratch
+        return float(np.median(ts))
 
+    return timed, per_launch, cold
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def cpu_baseline_chunked(ci, budget_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the chunked step:
+    absmax + quantize over the whole input, then each chunk conv and the
+    projection (conv + epilogue) at a random sample of their output positions,
+    each timed and scaled to all of its positions; TOPS of the whole step."""
+    import numpy as np
+    import oracle
+
+    spec = ci.spec
+    wq, ws = oracle.quantize_weights(ci.w)
+    wp, wps = oracle.quantize_weights(ci.w_proj)
+    t0 = time.perf_counter()
+    _, s, xq = oracle.act_absmax_quant(ci.x)
+    t_quant = time.perf_counter() - t0
+    launches = chunk_launches(spec)
+    total_ops = sum(L["ops"] for L in launches)
+    rng = np.random.default_rng(0)
+    per_budget = max(0.5, budget_s - t_quant) / len(launches)
+    t_total = t_quant
+    notes = []
+    for L in launches:
+        ls = L["spec"]
+        f0 = L["frame0"]
+        x_c = np.ascontiguousarray(xq[:, f0:f0 + ls.T])
+        cache = None if L["cache_frame0"] is None else np.ascontiguousarray(
+            xq[:, L["cache_frame0"]:L["cache_frame0"] + ls.k[0] - 1])
+        w_c, s_c, b_c = (wq, ws, ci.b) if L["name"] != "proj" else (wp, wps, ci.b_proj)
+        total = ls.positions
+        npos, used, t_conv = 32, 0, 0.0
+        while used < total and t_conv < per_budget:
+            pos = rng.integers(0, total, npos).astype(np.int64)
+            t1 = time.perf_counter()
+            acc = oracle.conv_acc(x_c, w_c, cache, positions=pos)
+            oracle.epilogue(acc, s, s_c, b_c)
+            t_conv += time.perf_counter() - t1
+            used += npos
+            npos = min(total - used, npos * 2) if used < total else 0
+            if npos <= 0:
+                break
+        t_total += t_conv / used * total
+        notes.append(f"{L['name']} {used} of {total} positions {t_conv:.2f} s")
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(total_ops / t_total / 1e12, 5), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "s_per_step": round(t_total, 2),
+            "sample": (f"absmax+quantize over all {spec.numel} elements ({t_quant:.2f} s); conv + epilogue at "
+                       f"random output positions of each launch, scaled to all of them: " + "; ".join(notes))}
+
+
+def bench_chunked(args):
+    """The chunked causal decode step (see the module docstring)."""
     import numpy as np
     import torch
 
     from w8a8_int8_quantized_act_amd import ops
     from w8a8_int8_quantized_act_amd import workloads as wl
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    ops.lib()
     dev = "cuda:0"
+    ci = wl.draw_workload(args.workload)[0]
+    spec = ci.spec
+    launches = chunk_launches(spec)
+    step_ops = sum(L["ops"] for L in launches)
+    conv3 = [L for L in launches if L["name"] != "proj"]
+    proj = [L for L in launches if L["name"] == "proj"]
 
+    x = torch.from_numpy(ci.x.view(np.int16)).to(dev).view(torch.bfloat16)
+    wq, ws = ops.quantize_weights(torch.from_numpy(ci.w).to(dev))
+    b = torch.from_numpy(ci.b).to(dev)
+    wp, wps = ops.quantize_weights(torch.from_numpy(ci.w_proj).to(dev))
+    bp = torch.from_numpy(ci.b_proj).to(dev)
+    absmax = torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=dev)
+    xs = torch.empty((1,), dtype=torch.float32, device=dev)
+    xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    y = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev)
+    yp = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.proj_cout), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    timed, per_launch, cold = _make_timer(stream)
+
+    # launch arguments marshalled once; the timed loops call the C entry points
+    # directly (the calls ops.* makes, without its per-call checks)
+    L = ops.lib()
+    P = ctypes.c_void_p
+    sp = P(stream.cuda_stream)
+    fx = spec.H * spec.W * spec.Cin            # int8 bytes per input frame (N = 1)
+    fy = spec.H * spec.W * spec.Cout * 2       # bf16 bytes per output frame
+    assert spec.N == 1
+    a_absmax = (P(x.data_ptr()), x.numel(), P(absmax.data_ptr()), sp)
+    a_quant = (P(x.data_ptr()), x.numel(), ctypes.c_float(1.0), P(absmax.data_ptr()), P(xs.data_ptr()),
+               P(xq.data_ptr()), sp)
+    conv_args = []
+    for Lc in conv3:
+        cs = Lc["spec"]
+        cache = None if Lc["cache_frame0"] is None else P(xq.data_ptr() + Lc["cache_frame0"] * fx)
+        conv_args.append((P(xq.data_ptr() + Lc["frame0"] * fx), P(xs.data_ptr()), cache, P(wq.data_ptr()),
+                          P(ws.data_ptr()), P(b.data_ptr()), cs.N, cs.T, cs.H, cs.W, cs.Cin, cs.Cout, 3, 3, 3,
+                          P(y.data_ptr() + Lc["frame0"] * fy), sp))
+    ps = proj[0]["spec"]
+    a_proj = (P(xq.data_ptr()), P(xs.data_ptr()), None, P(wp.data_ptr()), P(wps.data_ptr()), P(bp.data_ptr()),
+              ps.N, ps.T, ps.H, ps.W, ps.Cin, ps.Cout, 1, 1, 1, P(yp.data_ptr()), sp)
+    conv_fns = [(lambda a=a: L.qvae_causalconv3d_w8a8(*a)) for a in conv_args]
+
+    def absmax_pass():
+        return L.qvae_act_absmax(*a_absmax)
+
+    def quant_pass():
+        return L.qvae_act_quantize(*a_quant)
+
+    def chunk_convs():
+        rc = 0
+        for f in conv_fns:
+            rc |= f()
+        return rc
+
+    def proj_pass():
+        return L.qvae_causalconv3d_w8a8(*a_proj)
+
+    def step():
+        return absmax_pass() | quant_pass() | chunk_convs() | proj_pass()
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    assert step() == 0
+    torch.cuda.synchronize()
+    first_ms = (time.perf_counter() - t0) * 1e3
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    ms_per_step, ev_ms_per_step = timed(step, args.steps)
+    value = step_ops / (ms_per_step * 1e-3) / 1e12
+
+    # the dominant kernel: the four chunk convs back to back, K rounds
+    _, chunks_ms = timed(chunk_convs, args.steps)
+    conv_avg = chunks_ms / len(conv_fns)                       # average launch
+    ops_avg = sum(Lc["ops"] for Lc in conv3) / len(conv3)      # average algorithmic ops per launch
+    bytes_avg = sum(Lc["conv_bytes"] for Lc in conv3) / len(conv3)
+    conv_tops = ops_avg / (conv_avg * 1e-3) / 1e12
+    pl = per_launch(conv_fns, max(5, args.steps // 4))
+    per_chunk = {}
+    for Lc, d in zip(conv3, pl):
+        per_chunk[Lc["name"]] = {"alg_GOP": round(Lc["ops"] / 1e9, 2), "median_ms": round(_median(d), 5),
+                                 "min_ms": round(min(d), 5),
+                                 "TOPS_at_median": round(Lc["ops"] / (_median(d) * 1e-3) / 1e12, 1)}
+    _, proj_ms = timed(proj_pass, args.steps)
+    _, absmax_ms = timed(absmax_pass, args.steps)
+    _, quant_ms = timed(quant_pass, args.steps)
+    absmax_cold = cold(absmax_pass)
+    quant_cold = cold(quant_pass)
+
+    graph_ms = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gs = P(torch.cuda.current_stream().cuda_stream)
+            L.qvae_act_absmax(*(a_absmax[:-1] + (gs,)))
+            L.qvae_act_quantize(*(a_quant[:-1] + (gs,)))
+            for a in conv_args:
+                L.qvae_causalconv3d_w8a8(*(a[:-1] + (gs,)))
+            L.qvae_causalconv3d_w8a8(*(a_proj[:-1] + (gs,)))
+        g.replay()
+        torch.cuda.synchronize()
+        _, graph_ms = timed(lambda: (g.replay(), 0)[1], args.steps)
+    except Exception as exc:  # an extra figure, never the headline
+        print(f"graph replay skipped: {exc}", file=sys.stderr)
+
+    # output check after the timed loops: the chunked output equals one
+    # unchunked pass over all frames (no stale outputs counted)
+    ref_y = ops.causalconv3d_w8a8(xq, xs, wq, ws, b)
+    ref_p = ops.causalconv3d_w8a8(xq, xs, wp, wps, bp)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_y.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(ref_p.view(torch.int16), yp.view(torch.int16))
+
+    conv_src = os.path.join(ROOT, "w8a8_int8_quantized_act_amd", "csrc", "qvae_conv.hip")
+    traffic = read_traffic(args.workload, conv_src)
+    numel = spec.numel
+    attainable = min(PEAK_INT8_TOPS, ops_avg / bytes_avg * PEAK_HBM_GBS / 1e3)
+    pb = proj[0]["conv_bytes"]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "layer": (f"CausalConv3d 3x3x3 Cin=Cout={spec.Cin} input [{spec.N},{spec.Cin},{spec.T},{spec.H},"
+                      f"{spec.W}] bf16 channels-last as {spec.chunks} chunks of {spec.T // spec.chunks} frames "
+                      f"(chunks 1-{spec.chunks - 1} with the previous chunk's int8 frames as cache) + 1x1x1 "
+                      f"{spec.Cin}->{spec.proj_cout} projection on the same int8 input"),
+            "global_batch": spec.N,
+            "parallelism": "single GPU",
+            "step": ("absmax + quantize over all frames (one scale), 4 chunk convs, projection conv; each conv "
+                     "with fused FP32 rescale, bias, bf16 store"),
+            "alg_GOP_per_step": round(step_ops / 1e9, 2),
+        },
+        "roofline": {
+            "kernel": "k_conv_igemm 3x3x3 (the 4 chunk-conv launches of a step)",
+            "bound": "mfma",
+            "achieved": round(conv_tops, 2),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TOPS",
+            "op_kind": "INT8 ops, algorithmic count (structurally zero front-pad taps excluded)",
+            "frac": round(conv_tops / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+            "algorithmic_ops_per_launch": ops_avg,
+            "avg_launch_ms": round(conv_avg, 5),
+            "per_launch": per_chunk,
+            "algorithmic_bytes_per_launch": bytes_avg,
+            "ai_ops_per_byte": round(ops_avg / bytes_avg, 1),
+            "attainable_peak": round(attainable, 1),
+            "frac_of_attainable": round(conv_tops / attainable, 4),
+            "note": ("achieved = average algorithmic ops per chunk launch / average launch time of the 4 chunk "
+                     "convs run back to back (HIP events on the launch stream, K rounds); per_launch: one event "
+                     "pair around each launch, median and min over the rounds"),
+        },
+        "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
+        "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),
+        "chunk_convs_ms": round(chunks_ms, 5),
+        "projection": {"ms": round(proj_ms, 5), "alg_GOP": round(proj[0]["ops"] / 1e9, 2),
+                       "TOPS": round(proj[0]["ops"] / (proj_ms * 1e-3) / 1e12, 1),
+                       "GBs": round(pb / (proj_ms * 1e-3) / 1e9, 1),
+                       "frac_of_hbm": round(pb / (proj_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "quant_pass": {
+            "elements": numel,
+            "absmax_ms": round(absmax_ms, 5),
+            "absmax_GBs": round(2 * numel / (absmax_ms * 1e-3) / 1e9, 1),
+            "quantize_ms": round(quant_ms, 5),
+            "quantize_GBs": round(3 * numel / (quant_ms * 1e-3) / 1e9, 1),
+            "absmax_cold_ms": round(absmax_cold, 5),
+            "absmax_cold_GBs": round(2 * numel / (absmax_cold * 1e-3) / 1e9, 1),
+            "quantize_cold_ms": round(quant_cold, 5),
+            "quantize_cold_GBs": round(3 * numel / (quant_cold * 1e-3) / 1e9, 1),
+            "hbm_peak_GBs": PEAK_HBM_GBS,
+            "note": "absmax 2 B and quantize 3 B per element; *_ms: back-to-back launches (warm); *_cold: one "
+                    "launch after a 1 GiB write evicted the last-level cache, median of 10",
+        },
+        "first_call_ms": round(first_ms, 3),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline_chunked(ci, args.cpu_budget)
+    return out
+
+
+def bench_layer(args):
+    """One layer (``--workload``, ``--level``): absmax + quantize + conv."""
+    import numpy as np
+    import torch
+
+    from w8a8_int8_quantized_act_amd import ops
+    from w8a8_int8_quantized_act_amd import workloads as wl
+
+    dev = "cuda:0"
     ci = wl.draw_workload(args.workload, only=args.level)[-1]
     if args.frames and args.frames != ci.spec.T:
         spec_t = dataclasses.replace(ci.spec, T=args.frames, name=f"{ci.spec.name}_t{args.frames}")
         ci = wl.draw_conv(spec_t, torch.Generator().manual_seed(
             1000 * wl.WORKLOADS[args.workload].seed + 10 * args.level + args.frames))
-    variant = ci.spec.T != wl.WORKLOADS[args.workload].convs[args.level].T or args.clip != 1.0
     spec = ci.spec
     kt = spec.k[0]
     use_cache = spec.zero_cache
+    variant = (ci.spec.T != wl.WORKLOADS[args.workload].convs[args.level].T or args.clip != 1.0
+               or (use_cache and args.cache == "data"))
     cnt = layer_counts(spec, use_cache)
 
     x = torch.from_numpy(ci.x.view(np.int16)).to(dev).view(torch.bfloat16)
@@ -563,9 +735,8 @@ def main():
     y = torch.empty((spec.N, spec.T, spec.H, spec.W, spec.Cout), dtype=torch.bfloat16, device=dev)
     y_absmax = torch.empty((ops.ABSMAX_WORDS,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    timed, per_launch, cold = _make_timer(stream)
 
-    # Launch arguments marshalled once; the timed loops call the C entry
-    # points directly (the same calls ops.* makes, without its per-call checks).
     L = ops.lib()
     P = ctypes.c_void_p
     sp = P(stream.cuda_stream)
@@ -599,122 +770,46 @@ def main():
     def step():
         return absmax_pass() | quant_pass() | conv_pass()
 
-    # first call in this process (cold code object, cold caches)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     assert step() == 0
     torch.cuda.synchronize()
     first_ms = (time.perf_counter() - t0) * 1e3
-
+    if cache is not None and args.cache == "data":
+        # a cache of data instead of zeros: both cache frames hold the layer's
+        # own int8 codes (the distribution a real previous chunk would have)
+        cache.copy_(xq.expand(spec.N, kt - 1, spec.H, spec.W, spec.Cin) if spec.T == 1
+                    else xq[:, :1].expand(spec.N, kt - 1, spec.H, spec.W, spec.Cin))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    def timed(fn, k):
-        """k back-to-back launches on the stream, bracketed by synchronize and
-        by two HIP events on that stream -> (wall ms, event ms) per launch."""
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        e0.record(stream)
-        rc = 0
-        for _ in range(k):
-            rc |= fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        assert rc == 0
-        return wall * 1e3 / k, e0.elapsed_time(e1) / k
-
-    # timed region: exactly K steps
     ms_per_step, ev_ms_per_step = timed(step, args.steps)
     value = cnt["ops"] / (ms_per_step * 1e-3) / 1e12
-
-    # per kernel: K back-to-back launches each, on the launch stream
     _, conv_avg = timed(conv_pass, args.steps)
-    # the conv again in 5 groups of K/5 launches: median and min of the group averages
-    conv_groups = sorted(timed(conv_pass, max(1, args.steps // 5))[1] for _ in range(5))
+    pl = per_launch([conv_pass], max(5, args.steps // 4))[0]
     _, absmax_avg = timed(absmax_pass, args.steps)
     _, quant_avg = timed(quant_pass, args.steps)
     _, conv_mx_avg = timed(conv_absmax_pass, args.steps)
     ms_chained, _ = timed(step_chained, args.steps)
     conv_tops = cnt["ops"] / (conv_avg * 1e-3) / 1e12
-
-    # quant passes with a cold last-level cache: before each rep a 1 GiB
-    # scratch buffer is written on the same stream (evicting the 256 MB
-    # Infinity Cache), then one launch is bracketed by two events (the
-    # first fires when the fill has finished); median over the reps
-    def cold(fn, reps=10):
-        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ts = []
-        for i in range(reps):
-            scratch.fill_(i & 0xFF)
-            e0.record(stream)
-            assert fn() == 0
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        del scratch
-        return float(np.median(ts))
-
     absmax_cold = cold(absmax_pass)
     quant_cold = cold(quant_pass)
 
-    # the same step replayed from a HIP graph (launch overhead removed)
     graph_ms = None
     try:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            gs = torch.cuda.current_stream()
-            ga = (a_absmax[:-1] + (P(gs.cuda_stream),), a_quant[:-1] + (P(gs.cuda_stream),),
-                  a_conv[:-1] + (P(gs.cuda_stream),))
-            L.qvae_act_absmax(*ga[0])
-            L.qvae_act_quantize(*ga[1])
-            L.qvae_causalconv3d_w8a8(*ga[2])
+            gs = P(torch.cuda.current_stream().cuda_stream)
+            L.qvae_act_absmax(*(a_absmax[:-1] + (gs,)))
+            L.qvae_act_quantize(*(a_quant[:-1] + (gs,)))
+            L.qvae_causalconv3d_w8a8(*(a_conv[:-1] + (gs,)))
         g.replay()
         torch.cuda.synchronize()
         _, graph_ms = timed(lambda: (g.replay(), 0)[1], args.steps)
     except Exception as exc:  # graphs are an extra figure, never the headline
         print(f"graph replay skipped: {exc}", file=sys.stderr)
 
-    # The matrix cores' power-limited ceiling for this layer (after the timed
-    # region): the rate of the instruction the conv uses on random full-range
-    # codes and on zeros (qvae_probe_mfma), weighted by the share of K that
-    # reads the zero cache.  The frac against it says how close the conv is
-    # to what the chip sustains on these operands, not only to the nominal peak.
-    ceiling = None
-    try:
-        shape16 = spec.k[1] == 3 and (spec.Cin // 32) % 2 == 0 and spec.Cout % 192 == 0
-        pshape = 1 if shape16 else 0
-        gp = torch.Generator().manual_seed(13)
-        tabs = {"data": torch.randint(-127, 128, (14 * 4096 * 16,), generator=gp, dtype=torch.int8)
-                .view(torch.int32).reshape(14, 4096, 4).to(dev)}
-        tabs["zero"] = torch.zeros_like(tabs["data"])
-        iters = max(1, round(8e12 / (256 * 4 * ops.PROBE_WORK[pshape])))
-        rates = {}
-        for nm, tab in tabs.items():
-            ops.probe_mfma(pshape, tab, 50, 256)
-            torch.cuda.synchronize()
-            pts = []
-            for _ in range(5):
-                q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                q0.record(stream)
-                ops.probe_mfma(pshape, tab, iters, 256)
-                q1.record(stream)
-                torch.cuda.synchronize()
-                pts.append(q0.elapsed_time(q1))
-            rates[nm] = 256 * 4 * iters * ops.PROBE_WORK[pshape] / (sorted(pts)[2] * 1e-3) / 1e12
-        f_zero = zero_share_of_k(spec.T, spec.k[0], use_cache)
-        cap = 1.0 / ((1.0 - f_zero) / rates["data"] + f_zero / rates["zero"])
-        ceiling = {"instruction": "v_mfma_i32_16x16x64_i8" if shape16 else "v_mfma_i32_32x32x32_i8",
-                   "data_TOPS": round(rates["data"], 1), "zero_TOPS": round(rates["zero"], 1),
-                   "zero_share_of_K": round(f_zero, 4), "ceiling_TOPS": round(cap, 1),
-                   "frac_of_ceiling": round(conv_tops / cap, 4)}
-    except Exception as exc:  # an extra figure, never the headline
-        print(f"matrix-core ceiling probe skipped: {exc}", file=sys.stderr)
-
-    # output sanity after the timed loop (no stale-output speedups)
     ref_y = ops.causalconv3d_w8a8(xq, xs, wq, ws, b, cache)
     torch.cuda.synchronize()
     assert torch.equal(ref_y.view(torch.int16), y.view(torch.int16))
@@ -728,6 +823,15 @@ def main():
         wl_name += f" T={ci.spec.T}"
     if args.clip != 1.0:
         wl_name += f" clip={args.clip:g}"
+    if use_cache and args.cache == "data":
+        wl_name += " cache=data"
+    attainable = min(PEAK_INT8_TOPS, cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3)
+    cache_txt = ""
+    if use_cache:
+        cache_txt = ", explicit 2-frame cache of " + ("the layer's own int8 codes" if args.cache == "data"
+                                                      else "zeros")
+    else:
+        cache_txt = ", causal front padding"
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -744,32 +848,31 @@ def main():
         "config": {
             "workload": wl_name,
             "layer": f"CausalConv3d {spec.k[0]}x{spec.k[1]}x{spec.k[2]} Cin={spec.Cin} Cout={spec.Cout} "
-                     f"input [{spec.N},{spec.Cin},{spec.T},{spec.H},{spec.W}] bf16 channels-last"
-                     + (", explicit 2-frame zero cache" if use_cache else ", causal front padding"),
+                     f"input [{spec.N},{spec.Cin},{spec.T},{spec.H},{spec.W}] bf16 channels-last" + cache_txt,
             "global_batch": spec.N,
             "parallelism": "single GPU",
             "step": "absmax + quantize + implicit-GEMM conv (fused FP32 rescale, bias, bf16 store)",
+            "zero_share_of_K": round(zero_share_of_k(spec.T, kt, use_cache and args.cache == "zero"), 4),
         },
         "roofline": {
             "kernel": "k_conv_igemm",
-            "bound": "mfma",
+            "bound": "mfma" if attainable >= PEAK_INT8_TOPS else "hbm",
             "achieved": round(conv_tops, 2),
             "peak": PEAK_INT8_TOPS,
-            "unit": "TFLOP/s",
-            "op_kind": "INT8 ops (TOPS), algorithmic count",
+            "unit": "TOPS",
+            "op_kind": "INT8 ops, algorithmic count (structurally zero front-pad taps excluded)",
             "frac": round(conv_tops / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
             "algorithmic_ops_per_launch": cnt["ops"],
             "avg_launch_ms": round(conv_avg, 5),
-            "median_launch_ms": round(conv_groups[2], 5),
-            "min_launch_ms": round(conv_groups[0], 5),
+            "per_launch_median_ms": round(_median(pl), 5),
+            "per_launch_min_ms": round(min(pl), 5),
             "algorithmic_bytes_per_launch": cnt["conv_bytes"],
             "ai_ops_per_byte": round(cnt["ops"] / cnt["conv_bytes"], 1),
-            # the attainable roofline min(MFMA peak, AI x HBM bandwidth) for this layer
-            "attainable_peak": round(min(PEAK_INT8_TOPS, cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 1),
-            "frac_of_attainable": round(conv_tops / min(PEAK_INT8_TOPS,
-                                                        cnt["ops"] / cnt["conv_bytes"] * PEAK_HBM_GBS / 1e3), 4),
-            "power_limited_ceiling": ceiling,
+            "attainable_peak": round(attainable, 1),
+            "frac_of_attainable": round(conv_tops / attainable, 4),
+            "note": ("achieved = algorithmic ops / average launch time of K back-to-back launches (HIP events on "
+                     "the launch stream); per_launch_*: one event pair around each launch"),
         },
         "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
         "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),
@@ -777,6 +880,7 @@ def main():
         "conv_tops": round(conv_tops, 2),
         "nominal_ops": cnt["nominal_ops"],
         "quant_pass": {
+            "elements": spec.numel,
             "absmax_ms": round(absmax_avg, 5),
             "absmax_GBs": round(cnt["absmax_bytes"] / (absmax_avg * 1e-3) / 1e9, 1),
             "quantize_ms": round(quant_avg, 5),
@@ -786,9 +890,9 @@ def main():
             "quantize_cold_ms": round(quant_cold, 5),
             "quantize_cold_GBs": round(cnt["quant_bytes"] / (quant_cold * 1e-3) / 1e9, 1),
             "hbm_peak_GBs": PEAK_HBM_GBS,
-            "note": "absmax_/quantize_ms: back-to-back launches, warm (a tensor under 256 MB may be partly "
-                    "resident in the last-level cache); *_cold: one launch between two events after a 1 GiB "
-                    "write evicted the last-level cache, median of 10 (dispatch latency included)",
+            "note": "*_ms: back-to-back launches, warm (a tensor under 256 MB may be partly resident in the "
+                    "last-level cache); *_cold: one launch after a 1 GiB write evicted the last-level cache, "
+                    "median of 10 (dispatch latency included)",
         },
         "first_call_ms": round(first_ms, 3),
         "chained_step": {
@@ -800,8 +904,76 @@ def main():
         },
     }
     if not args.no_cpu:
-        cache_np = (np.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), np.int8) if use_cache else None)
+        cache_np = None
+        if use_cache:
+            cache_np = (np.zeros((spec.N, kt - 1, spec.H, spec.W, spec.Cin), np.int8) if args.cache == "zero"
+                        else cache.cpu().numpy())
         out["cpu_baseline"] = cpu_baseline(ci, cache_np, args.cpu_budget, args.clip)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="video_384_t8_chunked")
+    ap.add_argument("--level", type=int, default=0, help="layer index inside a level sweep")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--cache", choices=("zero", "data"), default="zero",
+                    help="layers with an explicit cache: all-zero codes (the workload) or the layer's own codes")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy (counter calibration)")
+    ap.add_argument("--first-calls", action="store_true",
+                    help="only time the first and second layer step at each resolution of the level sweeps")
+    ap.add_argument("--init", action="store_true", help="with --first-calls: call qvae_init first")
+    ap.add_argument("--frames", type=int, default=0,
+                    help="a multi-frame variant: the layer's shape with T frames (redrawn, same recipe)")
+    ap.add_argument("--clip", type=float, default=1.0,
+                    help="activation and weight clip ratio in (0, 1] (the page fixes 1.0)")
+    ap.add_argument("--decoder", action="store_true",
+                    help="only time the decoder's 28 residual-block convs per preset (W8A8 vs native bf16)")
+    ap.add_argument("--out-h", type=int, default=1024)
+    ap.add_argument("--out-w", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the W8A8 CausalConv3d path here runs on a single MI355X "
+              "(multi-GPU sharding is described, not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    if args.copy_probe:
+        import torch
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n, "launches": 3}))
+        return
+    if args.first_calls:
+        first_calls(with_init=args.init)
+        return
+    if args.decoder:
+        decoder_stack(args)
+        return
+
+    import torch
+
+    from w8a8_int8_quantized_act_amd import ops
+    from w8a8_int8_quantized_act_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ops.lib()
+    chunked = wl.WORKLOADS[args.workload].convs[0].chunks > 1
+    if chunked and (args.frames or args.clip != 1.0 or args.level):
+        print("--frames, --clip and --level apply to single-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    out = bench_chunked(args) if chunked else bench_layer(args)
     print(json.dumps(out))
 
 

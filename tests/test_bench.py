@@ -65,3 +65,27 @@ def test_zero_share_of_k():
     assert bench.zero_share_of_k(4, 3, True) == 3 / 12         # frames 0 and 1 read 2 and 1 cache taps
     assert bench.zero_share_of_k(8, 3, False) == 0.0           # no cache: padding taps are skipped
     assert bench.zero_share_of_k(1, 1, True) == 0.0            # a 1x1x1 conv has no temporal taps to pad
+
+
+def test_chunked_step_launches():
+    """The chunked decode step: 4 chunk convs of 2 frames (chunk 0 front-padded:
+    its frames see 1 and 2 temporal taps; chunks 1-3 read the previous chunk's
+    2 frames as cache: 3 taps each), then the 1x1x1 projection over all 8 frames."""
+    import bench
+    from w8a8_int8_quantized_act_amd import workloads as wl
+    spec = wl.WORKLOADS["video_384_t8_chunked"].convs[0]
+    ls = bench.chunk_launches(spec)
+    assert [L["name"] for L in ls] == ["chunk0", "chunk1", "chunk2", "chunk3", "proj"]
+    assert [L["frame0"] for L in ls] == [0, 2, 4, 6, 0]
+    assert [L["cache_frame0"] for L in ls] == [None, 0, 2, 4, None]
+    per_tap_frame = 2 * 384 * 384 * 9 * 90 * 160
+    assert [L["ops"] for L in ls[:4]] == [3 * per_tap_frame] + [6 * per_tap_frame] * 3
+    assert ls[4]["ops"] == 2 * 384 * 192 * 90 * 160 * 8
+    assert [round(L["ops"] / 1e9, 2) for L in ls] == [114.66, 229.32, 229.32, 229.32, 16.99]
+    px = 90 * 160
+    w3 = 384 * 384 * 27
+    assert ls[0]["conv_bytes"] == 2 * px * 384 + w3 + 8 * 384 + 2 * 384 * 2 * px
+    assert ls[1]["conv_bytes"] == 4 * px * 384 + w3 + 8 * 384 + 2 * 384 * 2 * px
+    assert ls[4]["conv_bytes"] == 8 * px * 384 + 384 * 192 + 8 * 192 + 2 * 192 * 8 * px
+    # the whole step: the 3x3x3 conv over 8 frames plus the projection
+    assert sum(L["ops"] for L in ls[:4]) == bench.layer_counts(spec, False)["ops"]

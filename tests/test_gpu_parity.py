@@ -548,3 +548,51 @@ def test_layer_causality_end_to_end(ops):
         assert f32_bits(s1.item()) == f32_bits(s2.item())
         assert torch.equal(y1[:, :t0 + 1].view(torch.int16), y2[:, :t0 + 1].view(torch.int16))
         assert not torch.equal(y1[:, t0 + 1:].view(torch.int16), y2[:, t0 + 1:].view(torch.int16))
+
+
+def test_init_loads_the_code_and_changes_nothing(ops):
+    """qvae_init (optional set-up) succeeds, may be repeated, and the calls
+    after it give the same results as before."""
+    ci, wq, ws, s, xq, cache = _small_inputs((1, 2, 9, 21, 64, 96, (3, 3, 3), True), 390)
+    args = (torch.from_numpy(xq).to(DEV), torch.tensor([s], device=DEV),
+            torch.from_numpy(pack_weight_codes(wq)).to(DEV), torch.from_numpy(ws).to(DEV),
+            torch.from_numpy(ci.b).to(DEV), torch.from_numpy(cache).to(DEV))
+    y0 = ops.causalconv3d_w8a8(*args)
+    ops.init()
+    ops.init()
+    y1 = ops.causalconv3d_w8a8(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.int16), y1.view(torch.int16))
+
+
+def test_binding_rejects_mismatched_buffers(ops):
+    """Caller-supplied outputs and per-channel vectors are checked (device,
+    dtype, shape or length) before the C call: the kernels size their stores
+    from the dimensions, not from the tensors."""
+    N, T, H, W, C = 1, 2, 8, 16, 64
+    x = torch.zeros((N, T, H, W, C), dtype=torch.bfloat16, device=DEV)
+    xq = torch.zeros((N, T, H, W, C), dtype=torch.int8, device=DEV)
+    wq, ws = ops.quantize_weights(torch.ones((C, C, 3, 3, 3), device=DEV) * 0.01)
+    am = torch.zeros((ops.ABSMAX_WORDS,), dtype=torch.int32, device=DEV)
+    xs = torch.ones((1,), dtype=torch.float32, device=DEV)
+    short_y = torch.empty((N, T, H, W - 1, C), dtype=torch.bfloat16, device=DEV)
+    f32_y = torch.empty((N, T, H, W, C), dtype=torch.float32, device=DEV)
+    bad_calls = [
+        lambda: ops.causalconv3d_w8a8_qin(x, am, wq, ws, out=short_y),
+        lambda: ops.causalconv3d_w8a8_qin(x, am, wq, ws, out=f32_y),
+        lambda: ops.causalconv3d_w8a8_qin(x, am, wq, ws, x_scale=torch.ones(1)),            # host scale
+        lambda: ops.causalconv3d_w8a8_qin(x, am, wq, ws[:C - 1]),
+        lambda: ops.causalconv3d_w8a8_acc32(xq, wq, out=torch.empty((N, T, H, W, C), dtype=torch.int16,
+                                                                    device=DEV)),
+        lambda: ops.causalconv3d_w8a8_acc32(xq, wq, out=torch.empty((N, T, H, W, C - 32), dtype=torch.int32,
+                                                                    device=DEV)),
+        lambda: ops.causalconv3d_w8a8(xq, xs, wq, ws, torch.zeros(C - 1, device=DEV)),       # short bias
+        lambda: ops.causalconv3d_w8a8(xq, xs, wq, ws[:C // 2]),                              # short w_scale
+        lambda: ops.causalconv3d_w8a8(xq, torch.ones(1), wq, ws),                            # host x_scale
+        lambda: ops.act_quantize(x, am, xq=torch.empty((N, T, H, W, C - 1), dtype=torch.int8, device=DEV)),
+        lambda: ops.act_absmax_quant(x, xq=torch.empty((N, T, H, W, C), dtype=torch.uint8, device=DEV)),
+    ]
+    for i, call in enumerate(bad_calls):
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(f"call {i} was accepted")

@@ -329,9 +329,9 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
     v4i wreg[C::PD][MA];
 
     // ---- prologue loads: the epilogue's factors (a few words, issued first
-    // so their latency hides under the rest), the weight ring, then the first
-    // stage's halo.  The factor products are formed only after the halo's
-    // wait, so no load waits for another.  The factors and biases of this
+    // so their latency hides under the rest), then the first stage's halo,
+    // then the weight ring.  The factor products are formed only after the
+    // halo's wait, so no load waits for another.  The factors and biases of this
     // tile's channels go to LDS with the first halo.
     constexpr int FPT = (C::BCO + NT - 1) / NT;
     float *s_fac = reinterpret_cast<float *>(smem + WORK);
@@ -1034,21 +1034,25 @@ static const void *conv_kernel(int mode, bool outmax)
 }
 
 // Workgroups of one instantiation that fit on a CU at once (registers, LDS,
-// waves), asked of the runtime once per instantiation.
+// waves), asked of the runtime once per instantiation and device (the
+// answer depends on the device's resources).
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>
 static int resident_per_cu(int mode, bool outmax)
 {
     using C = ConvCfg<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>;
-    static int occ[5] = {0, 0, 0, 0, 0};
+    static std::atomic<int> occ[kMaxDevices][5];   // 0 = not yet queried
     const int v = (mode == kModePlain && outmax) ? 4 : mode;
-    int &o = occ[v];
-    if (o == 0) {
-        int n = 0;
-        const void *f = conv_kernel<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(mode, outmax);
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, C::NT, 0) != hipSuccess || n < 1) n = 1;
-        o = n;
+    const int dev = current_device();
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    if (slot) {
+        const int o = occ[dev][v].load(std::memory_order_relaxed);
+        if (o > 0) return o;
     }
-    return o;
+    int n = 0;
+    const void *f = conv_kernel<WCO, WPX, WK, MB, NB, TH, TW, KH, KW, SPW>(mode, outmax);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, C::NT, 0) != hipSuccess || n < 1) n = 1;
+    if (slot) occ[dev][v].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 template <int WCO, int WPX, int WK, int MB, int NB, int TH, int TW, int KH, int KW, int SPW>

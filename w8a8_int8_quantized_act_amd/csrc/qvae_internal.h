@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <atomic>
 #include <stdlib.h>
 
 #include "qvae.h"
@@ -32,19 +33,34 @@ inline int launch_status()
     return e == hipSuccess ? QVAE_OK : QVAE_ELAUNCH;
 }
 
-// Compute units of the current device (queried once; 256 on MI355X).
+// Per-device caches: one slot per device id below kMaxDevices (larger ids are
+// queried on every call).  Slots are atomics, so concurrent first calls on
+// different threads each store the same value without a data race.
+constexpr int kMaxDevices = 64;
+
+// The current device's id, or -1 if the runtime cannot say.
+inline int current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    return dev;
+}
+
+// Compute units of the current device (queried once per device; 256 on MI355X).
 inline int device_cus()
 {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            cus = 256;
+    static std::atomic<int> cache[kMaxDevices];   // 0 = not yet queried
+    const int dev = current_device();
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    if (slot) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
     }
-    return cus;
+    int n = 0;
+    if (dev < 0 || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (slot) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // Load this translation unit's GPU code for the current device now instead of
@@ -54,7 +70,6 @@ int preload_act();
 int preload_wquant();
 int preload_conv();
 int preload_norm();
-int preload_probe();
 
 // ---- device helpers -------------------------------------------------------
 

@@ -88,8 +88,6 @@ def lib() -> ctypes.CDLL:
         L.qvae_rmsnorm_silu_absmax.restype = i32
         L.qvae_causalconv3d_w8a8_qin.argtypes = [P, P, P, f32, P, P, P] + [i32] * 9 + [P, P, P]
         L.qvae_causalconv3d_w8a8_qin.restype = i32
-        L.qvae_probe_mfma.argtypes = [i32, P, i32, i32, P, P]
-        L.qvae_probe_mfma.restype = i32
         L.qvae_init.argtypes = []
         L.qvae_init.restype = i32
         _lib = L
@@ -134,6 +132,27 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _vec(t: torch.Tensor | None, name: str, n: int, dtype=torch.float32):
+    """A per-channel device vector with at least n elements (None passes)."""
+    if t is None:
+        return None
+    _dev(t, name, dtype)
+    if t.numel() < n:
+        raise ValueError(f"{name} must hold at least {n} elements, got {t.numel()}")
+    return t
+
+
+def _out(t: torch.Tensor | None, name: str, shape, dtype, device):
+    """The caller's output tensor (checked: device, dtype, exact shape,
+    contiguous), or a new one."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name, dtype)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return t
 
 
@@ -209,8 +228,8 @@ def act_quantize(x: torch.Tensor, absmax_bits: torch.Tensor, clip_ratio: float =
     _dev(_bits_view(x), "x")
     if x_scale is None:
         x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
-    if xq is None:
-        xq = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    _vec(x_scale, "x_scale", 1)
+    xq = _out(xq, "xq", x.shape, torch.int8, x.device)
     _absmax_buf(absmax_bits)
     _check(lib().qvae_act_quantize(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                    _p(xq), _stream(stream)), "qvae_act_quantize")
@@ -227,8 +246,8 @@ def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None,
         absmax_bits = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=dev)
     if x_scale is None:
         x_scale = torch.empty((1,), dtype=torch.float32, device=dev)
-    if xq is None:
-        xq = torch.empty(x.shape, dtype=torch.int8, device=dev)
+    _vec(x_scale, "x_scale", 1)
+    xq = _out(xq, "xq", x.shape, torch.int8, dev)
     _absmax_buf(absmax_bits)
     _check(lib().qvae_act_absmax_quant(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                        _p(xq), _stream(stream)), "qvae_act_absmax_quant")
@@ -289,16 +308,10 @@ def causalconv3d_w8a8(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.Tensor,
                       out: torch.Tensor | None = None, stream=None):
     """xq int8 [N][T][H][W][Cin] -> y bf16 [N][T][H][W][Cout]."""
     N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
-    _dev(x_scale, "x_scale", torch.float32)
-    _dev(w_scale, "w_scale", torch.float32)
-    if bias is not None:
-        _dev(bias, "bias", torch.float32)
-    if out is None:
-        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=xq.device)
-    else:
-        _dev(out, "out", torch.bfloat16)
-        if tuple(out.shape) != (N, T, H, W, Cout):
-            raise ValueError("out shape")
+    _vec(x_scale, "x_scale", 1)
+    _vec(w_scale, "w_scale", Cout)
+    _vec(bias, "bias", Cout)
+    out = _out(out, "out", (N, T, H, W, Cout), torch.bfloat16, xq.device)
     _check(lib().qvae_causalconv3d_w8a8(_p(xq), _p(x_scale), _p(cache), _p(wq), _p(w_scale), _p(bias),
                                         N, T, H, W, Cin, Cout, kt, kh, kw, _p(out), _stream(stream)),
            "qvae_causalconv3d_w8a8")
@@ -312,16 +325,10 @@ def causalconv3d_w8a8_absmax(xq: torch.Tensor, x_scale: torch.Tensor, wq: torch.
     activation-maximum buffer -> (y, y_absmax); act_quantize(y, y_absmax)
     then quantizes y without its absmax pass."""
     N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
-    _dev(x_scale, "x_scale", torch.float32)
-    _dev(w_scale, "w_scale", torch.float32)
-    if bias is not None:
-        _dev(bias, "bias", torch.float32)
-    if out is None:
-        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=xq.device)
-    else:
-        _dev(out, "out", torch.bfloat16)
-        if tuple(out.shape) != (N, T, H, W, Cout):
-            raise ValueError("out shape")
+    _vec(x_scale, "x_scale", 1)
+    _vec(w_scale, "w_scale", Cout)
+    _vec(bias, "bias", Cout)
+    out = _out(out, "out", (N, T, H, W, Cout), torch.bfloat16, xq.device)
     if y_absmax is None:
         y_absmax = torch.empty((ABSMAX_WORDS,), dtype=torch.int32, device=xq.device)
     _absmax_buf(y_absmax, "y_absmax")
@@ -335,8 +342,7 @@ def causalconv3d_w8a8_acc32(xq: torch.Tensor, wq: torch.Tensor, cache: torch.Ten
                             out: torch.Tensor | None = None, stream=None):
     """Raw INT32 accumulators [N][T][H][W][Cout] (verification export)."""
     N, T, H, W, Cin, Cout, kt, kh, kw = _conv_dims(xq, wq, cache)
-    if out is None:
-        out = torch.empty((N, T, H, W, Cout), dtype=torch.int32, device=xq.device)
+    out = _out(out, "out", (N, T, H, W, Cout), torch.int32, xq.device)
     _check(lib().qvae_causalconv3d_w8a8_acc32(_p(xq), _p(cache), _p(wq), N, T, H, W, Cin, Cout, kt, kh, kw,
                                               _p(out), _stream(stream)), "qvae_causalconv3d_w8a8_acc32")
     return out
@@ -360,13 +366,12 @@ def causalconv3d_w8a8_qin(x: torch.Tensor, absmax_bits: torch.Tensor, wq: torch.
         _dev(cache, "cache", torch.bfloat16)
         if tuple(cache.shape) != (N, kt - 1, H, W, Cin):
             raise ValueError(f"cache must be [N][kt-1][H][W][Cin] = {(N, kt - 1, H, W, Cin)}")
-    _dev(w_scale, "w_scale", torch.float32)
-    if bias is not None:
-        _dev(bias, "bias", torch.float32)
-    if out is None:
-        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=x.device)
+    _vec(w_scale, "w_scale", Cout)
+    _vec(bias, "bias", Cout)
+    out = _out(out, "out", (N, T, H, W, Cout), torch.bfloat16, x.device)
     if x_scale is None:
         x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _vec(x_scale, "x_scale", 1)
     _absmax_buf(absmax_bits)
     _check(lib().qvae_causalconv3d_w8a8_qin(_p(x), _p(cache), _p(absmax_bits), float(clip_ratio), _p(wq),
                                             _p(w_scale), _p(bias), N, T, H, W, Cin, Cout, kt, kh, kw,
@@ -390,14 +395,8 @@ def causalconv3d_bf16(x: torch.Tensor, wp: torch.Tensor, bias: torch.Tensor | No
         _dev(cache, "cache", torch.bfloat16)
         if tuple(cache.shape) != (N, kt - 1, H, W, Cin):
             raise ValueError(f"cache must be [N][kt-1][H][W][Cin] = {(N, kt - 1, H, W, Cin)}")
-    if bias is not None:
-        _dev(bias, "bias", torch.float32)
-    if out is None:
-        out = torch.empty((N, T, H, W, Cout), dtype=torch.bfloat16, device=x.device)
-    else:
-        _dev(out, "out", torch.bfloat16)
-        if tuple(out.shape) != (N, T, H, W, Cout):
-            raise ValueError("out shape")
+    _vec(bias, "bias", Cout)
+    out = _out(out, "out", (N, T, H, W, Cout), torch.bfloat16, x.device)
     _check(lib().qvae_causalconv3d_bf16(_p(x), _p(cache), _p(wp), _p(bias), N, T, H, W, Cin, Cout, kt, kh, kw,
                                         _p(out), _stream(stream)), "qvae_causalconv3d_bf16")
     return out
@@ -411,26 +410,3 @@ def layer_forward(x: torch.Tensor, wq: torch.Tensor, w_scale: torch.Tensor, bias
     _, x_scale, xq = act_absmax_quant(x, clip_ratio, stream=stream)
     y = causalconv3d_w8a8(xq, x_scale, wq, w_scale, bias, cache, stream=stream)
     return y, x_scale, xq
-
-
-PROBE_SHAPES = {"i8_32x32x32": 0, "i8_16x16x64": 1, "bf16_32x32x16": 2, "bf16_16x16x32": 3}
-# work of one wave-round per shape (INT8 ops or bf16 flops)
-PROBE_WORK = {0: 24 * 65536, 1: 32 * 32768, 2: 24 * 32768, 3: 32 * 16384}
-
-
-def probe_mfma(shape: int, operands: torch.Tensor, iters: int, blocks: int, out: torch.Tensor | None = None,
-               stream=None) -> torch.Tensor:
-    """Matrix-core rate probe (measurement aid): `operands` int32 [14, 4096, 4]
-    on the device; returns the per-lane checksums.  The caller times it; the
-    work is blocks * 4 * iters * PROBE_WORK[shape]."""
-    _dev(operands, "operands", torch.int32)
-    if tuple(operands.shape) != (14, 4096, 4):
-        raise ValueError("operands must be int32 [14, 4096, 4]")
-    if out is None:
-        out = torch.empty(blocks * 256, dtype=torch.int32, device=operands.device)
-    _dev(out, "out", torch.int32)
-    if out.numel() < blocks * 256:
-        raise ValueError("out must hold blocks * 256 words")
-    _check(lib().qvae_probe_mfma(int(shape), _p(operands), int(iters), int(blocks), _p(out), _stream(stream)),
-           "qvae_probe_mfma")
-    return out
