@@ -42,7 +42,9 @@
 // A group of 8 values with such a quotient, or with |n| > 64 (where d grows
 // past the range the argument needs, up to infinity), is recomputed with the
 // correctly rounded division, so h equals bf16_rne(fl(n / d)) exactly for
-// this sequence's n and d.  The binary32 steps are within a few parts in 2^24
+// this sequence's n and d; values with n < -64 take n e^n instead (the
+// quotient's denominator overflows there while the value does not, see
+// silu_neg_tail).  The binary32 steps are within a few parts in 2^24
 // of the exact quantity, so h is the exact value rounded to bf16 or, when that
 // value lies that close to a bf16 rounding boundary, its neighbour.
 //
@@ -69,16 +71,17 @@ constexpr int kNormThreads = 256;
 constexpr int kNormWaves = kNormThreads / 64;
 constexpr int kNormMaxLoads = 16;   // 16-byte loads per lane per chunk: P * C / 8 <= 1024 (see norm_chunk_pixels)
 
-// exp(y) by the steps in the header (all binary32)
-__device__ __forceinline__ float exp_cw(float y)
+// exp(y) = p * 2^k by the steps in the header (all binary32): the mantissa
+// part p (in [0.7, 1.42]) and the exponent k
+__device__ __forceinline__ float exp_cw_parts(float y, int &k)
 {
     constexpr float kLog2e = 0x1.715476p+0f;
     constexpr float kLn2Hi = 0x1.62e4p-1f;         // 8 significant bits: k * kLn2Hi is exact
     constexpr float kLn2Lo = 0x1.7f7d1cp-20f;      // ln 2 - kLn2Hi
     y = fminf(fmaxf(y, -104.0f), 89.0f);
-    const float k = __builtin_rintf(y * kLog2e);
-    float r = __builtin_fmaf(k, -kLn2Hi, y);
-    r = __builtin_fmaf(k, -kLn2Lo, r);
+    const float kf = __builtin_rintf(y * kLog2e);
+    float r = __builtin_fmaf(kf, -kLn2Hi, y);
+    r = __builtin_fmaf(kf, -kLn2Lo, r);
     float p = 0x1.6c16c2p-10f;                     // 1/6!
     p = __builtin_fmaf(p, r, 0x1.111112p-7f);      // 1/5!
     p = __builtin_fmaf(p, r, 0x1.555556p-5f);      // 1/4!
@@ -86,7 +89,28 @@ __device__ __forceinline__ float exp_cw(float y)
     p = __builtin_fmaf(p, r, 0.5f);
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_amdgcn_ldexpf(p, (int)k);
+    k = (int)kf;
+    return p;
+}
+
+__device__ __forceinline__ float exp_cw(float y)
+{
+    int k;
+    const float p = exp_cw_parts(y, k);
+    return __builtin_amdgcn_ldexpf(p, k);
+}
+
+// SiLU(n) for n < -64, where n / (1 + exp(-n)) would overflow the
+// denominator below n = -88.7 and return -0 for values that are still
+// (sub)normal floats down to n ~ -103: n e^n / (1 + e^n) equals n e^n to
+// binary32 precision (e^n < 2^-92), formed as ldexp(n * p, k) with
+// e^n = p 2^k, so the one rounding into the subnormal range comes last
+// (denormals are kept, not flushed).
+__device__ __forceinline__ float silu_neg_tail(float n)
+{
+    int k;
+    const float p = exp_cw_parts(n, k);
+    return __builtin_amdgcn_ldexpf(n * p, k);
 }
 
 
@@ -205,7 +229,7 @@ __global__ __launch_bounds__(kNormThreads) void k_rmsnorm_silu(const uint16_t *_
             }
             if (!(namax <= 64.0f) || near.x <= 2 || near.y <= 2) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) qv[k] = nv[k] / dv[k];
+                for (int k = 0; k < 8; ++k) qv[k] = (nv[k] < -64.0f) ? silu_neg_tail(nv[k]) : nv[k] / dv[k];
             }
             uint32_t o[4];
 #pragma unroll
