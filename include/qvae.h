@@ -30,7 +30,8 @@
  * Conventions for every call:
  *   - pointers are DEVICE pointers (memory from hipMalloc / a torch CUDA
  *     tensor) unless stated otherwise; the caller allocates and frees every
- *     buffer, the library allocates nothing and keeps no per-call state;
+ *     buffer, the library allocates nothing and keeps no per-call state
+ *     (except qvae_act_absmax_quant_noalloc's static scratch array);
  *   - calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream) and never synchronize with the host;
  *   - layouts are channels-last: activations [N][T][H][W][C], contiguous;
@@ -45,7 +46,7 @@
  *     and the INT8 convolutions), so a caller's per-layer fallback to the
  *     native-precision convolution runs instead (the page's "disable" A/B);
  *   - concurrent calls on different streams are safe as long as their output
- *     buffers do not alias.
+ *     buffers do not alias (qvae_act_absmax_quant_noalloc: not on one GPU).
  */
 #ifndef QVAE_H
 #define QVAE_H
@@ -131,6 +132,26 @@ int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ratio,
 int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float clip_ratio,
                           uint32_t *absmax, float *x_scale, int8_t *xq,
                           void *stream);
+
+/*
+ * qvae_act_absmax_quant for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same two passes, the same codes, scale and maximum, but
+ * the QVAE_ABSMAX_WORDS activation-maximum words live in a static device
+ * array of the library instead of a caller's workspace (2052 bytes, one copy
+ * per GPU, held until the process ends).  The caller still passes x, x_scale
+ * and xq.  Allocates nothing on any call (the array's device address is
+ * looked up once per device, by qvae_init or by the first call on that
+ * device).  The array carries no state a call relies on; any numel that
+ * qvae_act_absmax_quant accepts is accepted (the partial maxima never need
+ * more than the array's 512 slots).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (on different streams) race and may
+ * return wrong scales; serialize them.  Same arguments and errors as
+ * qvae_act_absmax_quant, minus `absmax`; QVAE_ELAUNCH if the runtime cannot
+ * give the array's address.
+ */
+int qvae_act_absmax_quant_noalloc(const uint16_t *x, int64_t numel, float clip_ratio,
+                                  float *x_scale, int8_t *xq, void *stream);
 
 /*
  * The norm + SiLU pass in front of a decoder residual conv, h = SiLU(RMSNorm(x))

@@ -178,6 +178,40 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
 }
 
 
+// ---- the allocation-free entry point's scratch ------------------------------
+// qvae_act_absmax_quant_noalloc keeps its activation-maximum words (the same
+// QVAE_ABSMAX_WORDS words a caller's workspace holds for
+// qvae_act_absmax_quant) in this file-scope device array.  Every GPU the
+// library runs on holds its own copy, at its own address, until the process
+// ends.  On the host the name only stands in for the symbol; kernels get the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept here.  Nothing needs clearing between
+// calls: the absmax pass writes all of the partial words (0 where it has
+// nothing) and the quantize pass writes word 0.
+static __device__ __align__(256) uint32_t scratch[QVAE_ABSMAX_WORDS];
+
+static std::atomic<uint32_t *> g_scratch[kMaxDevices];   // per device id; nullptr = not looked up yet
+
+// The current device's copy of scratch, or nullptr if the runtime cannot give it.
+static uint32_t *scratch_on_device()
+{
+    const int dev = current_device();
+    const bool slot = dev >= 0 && dev < kMaxDevices;
+    if (slot) {
+        uint32_t *p = g_scratch[dev].load(std::memory_order_acquire);
+        if (p) return p;
+    }
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (slot) g_scratch[dev].store(static_cast<uint32_t *>(p), std::memory_order_release);
+    return static_cast<uint32_t *>(p);
+}
+
+int setup_scratch() { return scratch_on_device() ? QVAE_OK : QVAE_ELAUNCH; }
+
 int preload_act()
 {
     hipFuncAttributes attr;
@@ -232,4 +266,17 @@ extern "C" int qvae_act_absmax_quant(const uint16_t *x, int64_t numel, float cli
     int rc = qvae_act_absmax(x, numel, absmax, stream);
     if (rc != QVAE_OK) return rc;
     return qvae_act_quantize(x, numel, clip_ratio, absmax, x_scale, xq, stream);
+}
+
+extern "C" int qvae_act_absmax_quant_noalloc(const uint16_t *x, int64_t numel, float clip_ratio, float *x_scale,
+                                             int8_t *xq, void *stream)
+{
+    if (force_fail(true)) return QVAE_EFORCED;
+    if (!x || !x_scale || !xq || numel <= 0) return QVAE_EINVAL;
+    if (!aligned16(x) || !aligned16(xq)) return QVAE_EINVAL;
+    if (!(clip_ratio > 0.0f)) return QVAE_EINVAL;         // zero, negative or NaN
+    if (clip_ratio > 1.0f) return QVAE_EUNSUPPORTED;
+    uint32_t *ws = scratch_on_device();
+    if (!ws) return QVAE_ELAUNCH;
+    return qvae_act_absmax_quant(x, numel, clip_ratio, ws, x_scale, xq, stream);
 }

@@ -70,6 +70,9 @@ int preload_act();
 int preload_wquant();
 int preload_conv();
 int preload_norm();
+// Look up the current device's copy of the allocation-free entry point's
+// scratch array (qvae_act.hip); QVAE_OK or QVAE_ELAUNCH.  Used by qvae_init.
+int setup_scratch();
 
 // ---- device helpers -------------------------------------------------------
 

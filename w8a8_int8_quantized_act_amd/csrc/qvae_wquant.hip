@@ -147,7 +147,7 @@ extern "C" int qvae_version(void) { return (0 << 16) | 3; }
 extern "C" int qvae_init(void)
 {
     (void)device_cus();
-    const int r[] = {preload_act(), preload_wquant(), preload_conv(), preload_norm()};
+    const int r[] = {preload_act(), preload_wquant(), preload_conv(), preload_norm(), setup_scratch()};
     for (int v : r)
         if (v != QVAE_OK) return v;
     return QVAE_OK;

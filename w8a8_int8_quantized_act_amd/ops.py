@@ -12,6 +12,7 @@ Names follow the C entry points:
   act_absmax              -> qvae_act_absmax
   act_quantize            -> qvae_act_quantize
   act_absmax_quant        -> qvae_act_absmax_quant
+  act_absmax_quant_noalloc -> qvae_act_absmax_quant_noalloc
   causalconv3d_w8a8       -> qvae_causalconv3d_w8a8
   causalconv3d_w8a8_acc32 -> qvae_causalconv3d_w8a8_acc32
   causalconv3d_w8a8_absmax -> qvae_causalconv3d_w8a8_absmax
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
         L.qvae_act_quantize.restype = i32
         L.qvae_act_absmax_quant.argtypes = [P, i64, f32, P, P, P, P]
         L.qvae_act_absmax_quant.restype = i32
+        L.qvae_act_absmax_quant_noalloc.argtypes = [P, i64, f32, P, P, P]
+        L.qvae_act_absmax_quant_noalloc.restype = i32
         L.qvae_causalconv3d_w8a8.argtypes = [P, P, P, P, P, P] + [i32] * 9 + [P, P]
         L.qvae_causalconv3d_w8a8.restype = i32
         L.qvae_causalconv3d_w8a8_absmax.argtypes = [P, P, P, P, P, P] + [i32] * 9 + [P, P, P]
@@ -252,6 +255,20 @@ def act_absmax_quant(x: torch.Tensor, clip_ratio: float = 1.0, absmax_bits=None,
     _check(lib().qvae_act_absmax_quant(_p(x), x.numel(), float(clip_ratio), _p(absmax_bits), _p(x_scale),
                                        _p(xq), _stream(stream)), "qvae_act_absmax_quant")
     return absmax_bits, x_scale, xq
+
+
+def act_absmax_quant_noalloc(x: torch.Tensor, clip_ratio: float = 1.0, x_scale=None, xq=None, stream=None):
+    """qvae_act_absmax_quant_noalloc: both passes with the activation-maximum
+    words in the library's static scratch (no workspace; with x_scale and xq
+    given, nothing is allocated) -> (x_scale float32 [1], xq int8 of x's shape)."""
+    _dev(_bits_view(x), "x")
+    if x_scale is None:
+        x_scale = torch.empty((1,), dtype=torch.float32, device=x.device)
+    _vec(x_scale, "x_scale", 1)
+    xq = _out(xq, "xq", x.shape, torch.int8, x.device)
+    _check(lib().qvae_act_absmax_quant_noalloc(_p(x), x.numel(), float(clip_ratio), _p(x_scale), _p(xq),
+                                               _stream(stream)), "qvae_act_absmax_quant_noalloc")
+    return x_scale, xq
 
 
 # ------------------------------------------------------------------ norm + SiLU prologue
