@@ -121,7 +121,10 @@ constexpr int kStoreNT = 2;
 
 // Halo pixels are stored with a 48-byte pitch (32 data bytes + 16 unused):
 // 3 is odd, so 16 consecutive pixels read by 16 consecutive lanes hit 16
-// distinct 16-byte bank groups.
+// distinct 16-byte bank groups.  (Measured with the LDS bank-conflict
+// counter: the 32x32 tiles' B reads are conflict-free; the 16x16 tiles'
+// pattern, the same pixels' second 16 bytes in lanes 16-31 and the second
+// slice in lanes 32-63, takes twice the LDS cycles per read.)
 constexpr int kHaloPitch = 48;
 
 // (QCFG: the input-quantizing conv's configuration, see M16 and HD; ACC32_:
