@@ -438,6 +438,24 @@ def _make_timer(stream):
     return timed, per_launch, cold
 
 
+def copy_reference(timed, cold, dev, nbytes=1 << 28):
+    """Read+write rate of a plain device-to-device copy of nbytes on this machine
+    (torch's copy kernel), warm (back-to-back) and cold: the practical ceiling
+    for a pass that both reads and writes HBM."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    def cp():
+        dst.copy_(src)
+        return 0
+    cp()
+    _, warm = timed(cp, 20)
+    c = cold(cp)
+    del src, dst
+    return {"bytes_read_plus_written": 2 * nbytes, "warm_GBs": round(2 * nbytes / (warm * 1e-3) / 1e9, 1),
+            "cold_GBs": round(2 * nbytes / (c * 1e-3) / 1e9, 1)}
+
+
 def _median(v):
     v = sorted(v)
     n = len(v)
@@ -600,6 +618,7 @@ def bench_chunked(args):
     _, quant_ms = timed(quant_pass, args.steps)
     absmax_cold = cold(absmax_pass)
     quant_cold = cold(quant_pass)
+    copy_ref = copy_reference(timed, cold, dev)
 
     graph_ms = None
     try:
@@ -693,8 +712,10 @@ def bench_chunked(args):
             "quantize_cold_ms": round(quant_cold, 5),
             "quantize_cold_GBs": round(3 * numel / (quant_cold * 1e-3) / 1e9, 1),
             "hbm_peak_GBs": PEAK_HBM_GBS,
+            "reference_copy_256MiB": copy_ref,
             "note": "absmax 2 B and quantize 3 B per element; *_ms: back-to-back launches (warm); *_cold: one "
-                    "launch after a 1 GiB write evicted the last-level cache, median of 10",
+                    "launch after a 1 GiB write evicted the last-level cache, median of 10; reference_copy: a "
+                    "plain device copy on the same box (read + written bytes), the ceiling for a read+write pass",
         },
         "first_call_ms": round(first_ms, 3),
     }
