@@ -14,8 +14,17 @@ quantization happens once at load, outside the timed region.
 Prints ONE JSON line.  ``value`` is INT8 TOPS of the whole step (algorithmic
 conv ops / step time); the ``roofline`` object covers the dominant kernel
 (the 3x3x3 conv: the four chunk launches), timed with HIP events around its
-launches on the stream it runs on; ``cpu_baseline`` is the CPU oracle on a
-bounded sample of the same workload.
+launches inside K steps run right after the timed ones, on the stream it runs
+on; ``cpu_baseline`` is the CPU oracle on a bounded sample of the same
+workload.
+
+Order of the chunked run: the first call, the per-kernel figures (each
+kernel on its own, warm and cold, a plain copy, the captured step), then the
+W warm-up steps and the K timed steps, K steps with events around the chunk
+convs, and K more steps after one second idle.  The chip's power management needs a few tens of milliseconds of
+sustained load to settle after any idle period (the steps right after it run
+up to ~30 % slower), so the headline steps follow the per-kernel figures
+without a pause, and the after-idle figure is reported beside them.
 """
 from __future__ import annotations
 
@@ -518,6 +527,29 @@ def cpu_baseline_chunked(ci, budget_s=12.0):
                        f"random output positions of each launch, scaled to all of them: " + "; ".join(notes))}
 
 
+def step_series(step, stream, n):
+    """Durations of n consecutive steps (an event pair around each, on the
+    stream), right after the first call, then again after 1 s and after 5 s
+    with the GPU idle: means over windows of 100 steps and the first 10."""
+    import numpy as np
+    import torch
+    out = {"steps_per_phase": n}
+    for phase, gap in (("from_first_call", 0.0), ("after_1s_idle", 1.0), ("after_5s_idle", 5.0)):
+        time.sleep(gap)
+        ev = _events(n + 1)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(n):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        d = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)]) * 1e3
+        out[phase] = {"us_per_step_100_step_windows": [round(float(d[i:i + 100].mean()), 1) for i in range(0, n, 100)],
+                      "us_first_10_steps": [round(float(v), 1) for v in d[:10]],
+                      "us_median_last_half": round(float(np.median(d[n // 2:])), 1)}
+    return out
+
+
 def bench_chunked(args):
     """The chunked causal decode step (see the module docstring)."""
     import numpy as np
@@ -593,26 +625,19 @@ def bench_chunked(args):
     assert step() == 0
     torch.cuda.synchronize()
     first_ms = (time.perf_counter() - t0) * 1e3
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    if args.series:
+        return step_series(step, stream, args.series)
 
-    # timed region: exactly K steps
-    ms_per_step, ev_ms_per_step = timed(step, args.steps)
-    value = step_ops / (ms_per_step * 1e-3) / 1e12
-
-    # the dominant kernel: the four chunk convs back to back, K rounds
-    _, chunks_ms = timed(chunk_convs, args.steps)
-    conv_avg = chunks_ms / len(conv_fns)                       # average launch
-    ops_avg = sum(Lc["ops"] for Lc in conv3) / len(conv3)      # average algorithmic ops per launch
-    bytes_avg = sum(Lc["conv_bytes"] for Lc in conv3) / len(conv3)
-    conv_tops = ops_avg / (conv_avg * 1e-3) / 1e12
+    # per-kernel figures first: each kernel on its own, warm and cold, a plain
+    # device copy, the captured step.  They also give the GPU the sustained
+    # load its clock needs to settle before the timed steps.
     pl = per_launch(conv_fns, max(5, args.steps // 4))
     per_chunk = {}
     for Lc, d in zip(conv3, pl):
         per_chunk[Lc["name"]] = {"alg_GOP": round(Lc["ops"] / 1e9, 2), "median_ms": round(_median(d), 5),
                                  "min_ms": round(min(d), 5),
                                  "TOPS_at_median": round(Lc["ops"] / (_median(d) * 1e-3) / 1e12, 1)}
+    _, loop_ms = timed(chunk_convs, max(args.steps, 50))       # the 4 chunk convs back to back
     _, proj_ms = timed(proj_pass, args.steps)
     _, absmax_ms = timed(absmax_pass, args.steps)
     _, quant_ms = timed(quant_pass, args.steps)
@@ -635,6 +660,37 @@ def bench_chunked(args):
         _, graph_ms = timed(lambda: (g.replay(), 0)[1], args.steps)
     except Exception as exc:  # an extra figure, never the headline
         print(f"graph replay skipped: {exc}", file=sys.stderr)
+
+    # the headline: W warm-up steps, then exactly K timed steps
+    for _ in range(args.warmup):
+        step()
+    ms_per_step, ev_ms_per_step = timed(step, args.steps)
+    value = step_ops / (ms_per_step * 1e-3) / 1e12
+
+    # right after them, K more steps, each with an event pair around its four
+    # chunk convs (same stream): the dominant kernel's average launch inside
+    # the steps.  (An event record between two kernels costs the queue a few
+    # microseconds, so the headline steps above carry none.)
+    chunk_ev = [_events(2) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    rc = 0
+    for k in range(args.steps):
+        rc |= absmax_pass() | quant_pass()
+        chunk_ev[k][0].record(stream)
+        rc |= chunk_convs()
+        chunk_ev[k][1].record(stream)
+        rc |= proj_pass()
+    torch.cuda.synchronize()
+    assert rc == 0
+    chunks_ms = sum(a.elapsed_time(b) for a, b in chunk_ev) / args.steps
+    conv_avg = chunks_ms / len(conv_fns)                       # average launch inside the timed steps
+    ops_avg = sum(Lc["ops"] for Lc in conv3) / len(conv3)      # average algorithmic ops per launch
+    bytes_avg = sum(Lc["conv_bytes"] for Lc in conv3) / len(conv3)
+    conv_tops = ops_avg / (conv_avg * 1e-3) / 1e12
+
+    # the same K steps after one second with the GPU idle (the clock's transient)
+    time.sleep(1.0)
+    idle_ms, _ = timed(step, args.steps)
 
     # output check after the timed loops: the chunked output equals one
     # unchunked pass over all frames (no stale outputs counted)
@@ -691,11 +747,15 @@ def bench_chunked(args):
             "attainable_peak": round(attainable, 1),
             "frac_of_attainable": round(conv_tops / attainable, 4),
             "note": ("achieved = average algorithmic ops per chunk launch / average launch time of the 4 chunk "
-                     "convs run back to back (HIP events on the launch stream, K rounds); per_launch: one event "
-                     "pair around each launch, median and min over the rounds"),
+                     "convs inside K steps run right after the timed ones (one HIP event pair around the 4 "
+                     "launches of each step, on the launch stream); per_launch: one event pair around each "
+                     "launch, run before the timed steps, median and min over the rounds; chunk_loop_ms: the 4 "
+                     "launches back to back, before the timed steps"),
+            "chunk_loop_ms": round(loop_ms, 5),
         },
         "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
         "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),
+        "ms_per_step_after_1s_idle": round(idle_ms, 5),
         "chunk_convs_ms": round(chunks_ms, 5),
         "projection": {"ms": round(proj_ms, 5), "alg_GOP": round(proj[0]["ops"] / 1e9, 2),
                        "TOPS": round(proj[0]["ops"] / (proj_ms * 1e-3) / 1e12, 1),
@@ -957,6 +1017,9 @@ def main():
                     help="only time the decoder's 28 residual-block convs per preset (W8A8 vs native bf16)")
     ap.add_argument("--out-h", type=int, default=1024)
     ap.add_argument("--out-w", type=int, default=1024)
+    ap.add_argument("--series", type=int, default=0,
+                    help="chunked workload only: the duration of each of N steps from the first call on, then of "
+                         "N more after 1 s and after 5 s idle (the clock's transient), instead of the bench line")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -993,6 +1056,9 @@ def main():
     chunked = wl.WORKLOADS[args.workload].convs[0].chunks > 1
     if chunked and (args.frames or args.clip != 1.0 or args.level):
         print("--frames, --clip and --level apply to single-layer workloads", file=sys.stderr)
+        sys.exit(2)
+    if args.series and not chunked:
+        print("--series applies to the chunked workload", file=sys.stderr)
         sys.exit(2)
     out = bench_chunked(args) if chunked else bench_layer(args)
     print(json.dumps(out))
