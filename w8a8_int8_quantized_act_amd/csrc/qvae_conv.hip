@@ -122,9 +122,9 @@ constexpr int kStoreNT = 2;
 // Halo pixels are stored with a 48-byte pitch (32 data bytes + 16 unused):
 // 3 is odd, so 16 consecutive pixels read by 16 consecutive lanes hit 16
 // distinct 16-byte bank groups.  (Measured with the LDS bank-conflict
-// counter: the 32x32 tiles' B reads are conflict-free; the 16x16 tiles'
-// pattern, the same pixels' second 16 bytes in lanes 16-31 and the second
-// slice in lanes 32-63, takes twice the LDS cycles per read.)
+// counter: the 32x32 tiles' B reads, 32 pixels in lanes 0-31 and the same
+// pixels' second 16 bytes in lanes 32-63, are conflict-free; for the 16x16
+// tiles see SLICE_BYTES and b_q0.)
 constexpr int kHaloPitch = 48;
 
 // (QCFG: the input-quantizing conv's configuration, see M16 and HD; ACC32_:
@@ -170,9 +170,15 @@ struct ConvCfg {
     static constexpr int HALO_STORE_STEP = (QCFG && PD < KS) ? PD : KS - 1;
     static constexpr int HH = TH + KH - 1;
     static constexpr int HWD = TW + KW - 1;
-    // one 32-channel slice of the halo; slices are 32 bytes apart modulo 128
-    // so the chunks of one pixel written by consecutive lanes spread over banks
-    static constexpr int SLICE_BYTES = (HH * HWD * kHaloPitch + 127) / 128 * 128 + 32;
+    // one 32-channel slice of the halo.  32x32 tiles: slices 32 bytes apart
+    // modulo 128, so the chunks of one pixel written by consecutive lanes
+    // spread over banks.  16x16 tiles: slices a multiple of 256 bytes apart,
+    // which with the lane groups of their B reads (see b_q0) makes those
+    // reads conflict-free (measured with the LDS bank-conflict counter: any
+    // other distance modulo 256, or the other assignment of lane groups to
+    // slices, costs every such read twice the LDS cycles)
+    static constexpr int SLICE_BYTES = M16 ? (HH * HWD * kHaloPitch + 16 + 255) / 256 * 256
+                                           : (HH * HWD * kHaloPitch + 127) / 128 * 128 + 32;
     // the padding after slice 0's pixels, never read: the halo stores of lanes
     // without a chunk go there so the store loop needs no branch
     static constexpr int HALO_PAD = HH * HWD * kHaloPitch;
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
     // arithmetic.
     // With 16x16 tiles, lane (r, g) = (lane % 16, lane / 16) of the operand of
     // channels 16 h .. 16 h + 15 of a 32-channel block takes the 16 bytes that
-    // lane r + 16 h + 32 (g % 2) holds in the fragment of slice g / 2 (KHW
+    // lane r + 16 h + 32 (g / 2) holds in the fragment of slice g % 2 (KHW
     // fragments further on): row r + 16 h, the same k values.  The k value
     // behind each (lane group, byte) is the same function for A and B (the B
     // reads below pair it the same way), so the product covers the 64 k of the
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
     const int cb_stride = kt * S * C::KHW * 1024;          // bytes per 32-channel block (< 2^23)
     const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<int8_t *>(a.wq) + (size_t)(co0 / 32 + wco * MB) * cb_stride, 0, MB * cb_stride, 0x00020000);
-    const int wlane = M16 ? ((lane >> 5) * C::KHW * 1024 + ((lane & 15) + 32 * ((lane >> 4) & 1)) * 16) : lane * 16;
+    const int wlane = M16 ? (((lane >> 4) & 1) * C::KHW * 1024 + ((lane & 15) + 32 * (lane >> 5)) * 16) : lane * 16;
     auto wstage = [&](const Tile &tl, int st) -> int {
         const int it = st / nsp;
         const int p = st - it * nsp;
@@ -479,16 +485,18 @@ __global__ __launch_bounds__(WCO *WPX *WK * 64, (WK == 1 && MB * NB < 9) ? 2 : 1
 
     // B fragment base offsets (pixel of lane, within the stage buffer).  32x32
     // tiles: lane (lrow, lhalf) reads 16 bytes lhalf of pixel lrow of the block.
-    // 16x16 tiles: lane (r, g) reads 16 bytes g % 2 of slice g / 2 of pixel r,
-    // the k values the weight operand's lane group g holds.
+    // 16x16 tiles: lane (r, g) reads 16 bytes g / 2 of slice g % 2 of pixel r,
+    // the k values the weight operand's lane group g holds (lanes 0-15 and
+    // 16-31 read the two slices at the same bank offsets, lanes 32-63 the same
+    // pixels 16 bytes further on).
     int b_q0[NA];
 #pragma unroll
     for (int nb = 0; nb < NA; ++nb) {
         if constexpr (M16) {
             const int p = (wpx * NA + nb) * 16 + (lane & 15);
             const int pr = p / TW, pc = p - pr * TW;
-            b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + ((lane >> 4) & 1) * 16 +
-                       ((lane >> 5) + wk * C::SPW) * C::SLICE_BYTES;
+            b_q0[nb] = (pr * C::HWD + pc) * kHaloPitch + (lane >> 5) * 16 +
+                       (((lane >> 4) & 1) + wk * C::SPW) * C::SLICE_BYTES;
         } else {
             const int p = (wpx * NB + nb) * 32 + lrow;
             const int pr = p / TW, pc = p - pr * TW;
