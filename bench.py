@@ -18,13 +18,14 @@ launches inside K steps run right after the timed ones, on the stream it runs
 on; ``cpu_baseline`` is the CPU oracle on a bounded sample of the same
 workload.
 
-Order of the chunked run: the first call, the per-kernel figures (each
-kernel on its own, warm and cold, a plain copy, the captured step), then the
-W warm-up steps and the K timed steps, K steps with events around the chunk
-convs, and K more steps after one second idle.  The chip's power management needs a few tens of milliseconds of
-sustained load to settle after any idle period (the steps right after it run
-up to ~30 % slower), so the headline steps follow the per-kernel figures
-without a pause, and the after-idle figure is reported beside them.
+Order of the chunked run: the first call, the step untimed for 150 ms, the
+per-kernel figures (each kernel on its own, warm and cold, a plain copy, the
+captured step), then the W warm-up steps and the K timed steps, K steps with
+events around the chunk convs, and K more steps after one second idle.  The
+chip's power management needs a few tens of milliseconds of sustained load to
+settle after any idle period (the steps right after it run up to ~35 %
+slower), so everything timed follows that settling load without a pause, and
+the after-idle figure is reported beside the headline.
 """
 from __future__ import annotations
 
@@ -628,9 +629,17 @@ def bench_chunked(args):
     if args.series:
         return step_series(step, stream, args.series)
 
-    # per-kernel figures first: each kernel on its own, warm and cold, a plain
-    # device copy, the captured step.  They also give the GPU the sustained
-    # load its clock needs to settle before the timed steps.
+    # the step, untimed, for at least 150 ms: the clock settles under sustained
+    # load after the idle start.  Then the per-kernel figures (each kernel on
+    # its own, warm and cold, a plain device copy, the captured step), which
+    # keep the load on until the timed steps.
+    t_end = time.perf_counter() + 0.15
+    settle_steps = 0
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            step()
+        settle_steps += 10
+        torch.cuda.synchronize()
     pl = per_launch(conv_fns, max(5, args.steps // 4))
     per_chunk = {}
     for Lc, d in zip(conv3, pl):
@@ -756,6 +765,7 @@ def bench_chunked(args):
         "ms_per_step_gpu_events": round(ev_ms_per_step, 5),
         "ms_per_step_hip_graph": None if graph_ms is None else round(graph_ms, 5),
         "ms_per_step_after_1s_idle": round(idle_ms, 5),
+        "settle_steps": settle_steps,
         "chunk_convs_ms": round(chunks_ms, 5),
         "projection": {"ms": round(proj_ms, 5), "alg_GOP": round(proj[0]["ops"] / 1e9, 2),
                        "TOPS": round(proj[0]["ops"] / (proj_ms * 1e-3) / 1e12, 1),
