@@ -74,6 +74,15 @@ def test_act_quant_sizes(ops, n):
     _check_act(ops, _bits_of(torch.randn(n, generator=g) * 3))
 
 
+@pytest.mark.parametrize("n", [(16 << 20) - 3, (16 << 20) + 11])
+def test_act_quant_both_store_policies(ops, n):
+    # the quantize pass stores the codes of tensors from 16 Mi elements on with
+    # the default cache policy and smaller ones non-temporally: both sides of
+    # that size, bit-exact against the oracle
+    g = torch.Generator().manual_seed(200 + n % 89)
+    _check_act(ops, _bits_of(torch.randn(n, generator=g) * 3))
+
+
 def test_act_quant_outliers_large(ops):
     g = torch.Generator().manual_seed(101)
     x = torch.randn(3_000_011, generator=g)

@@ -91,19 +91,33 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
         for (int k = gridDim.x + threadIdx.x; k < kAbsmaxParts; k += kAbsmaxThreads) partials[k] = 0;
 }
 
-// 8 codes, non-temporal (nothing here reads them again; measured 2-10 % faster
-// for the pass than the default cache policy)
+// 8 codes.  NT: non-temporal (the pass alone runs 2-10 % faster that way);
+// otherwise the default policy, which leaves the codes in the last-level cache
+// for the conv that reads them next (see kCachedCodesMin).
+template <bool NT>
 __device__ __forceinline__ void store_codes(uint2 *dst, uint2 v)
 {
     typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
-    __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t *>(dst));
+    if constexpr (NT)
+        __builtin_nontemporal_store(u32x2_t{v.x, v.y}, reinterpret_cast<u32x2_t *>(dst));
+    else
+        *reinterpret_cast<u32x2_t *>(dst) = u32x2_t{v.x, v.y};
 }
 
 constexpr int kQuantThreads = 256;
 constexpr int kQuantUnroll = 4;   // 16-byte loads in flight per lane
 
+// From this many elements on, the codes are stored with the default cache
+// policy: the consumer's reads then hit the last-level cache, which outweighs
+// the slower pass (measured with the codes' consumer, the conv, right after:
+// layer steps at 25, 50 and 100 M elements 1, 4 and 8 % faster, the chunked
+// decode step at 44 M ~2 % faster; at 6.3 M elements the step is ~2.5 % faster
+// with non-temporal stores, so smaller tensors keep them).
+constexpr int64_t kCachedCodesMin = 16 << 20;
+
 // Each lane: 8 bf16 per 16-byte load -> 8 codes per 8-byte store; a wave's
 // load instruction covers 1 KB of contiguous input.
+template <bool NT>
 __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restrict__ x16,
                                                            int64_t n16,   // groups of 8 elements
                                                            const uint16_t *__restrict__ x,
@@ -159,7 +173,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
         // issues all its loads before its first store
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u)
-            if (i + u * stride < n16) store_codes(&q8[i + u * stride], quant8(v0[u], s, r, exact_only));
+            if (i + u * stride < n16) store_codes<NT>(&q8[i + u * stride], quant8(v0[u], s, r, exact_only));
         for (i += kQuantUnroll * stride; i < n16; i += kQuantUnroll * stride) {
             u32x4 v[kQuantUnroll];
 #pragma unroll
@@ -167,7 +181,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quantize(const u32x4 *__restr
                 v[u] = (i + u * stride < n16) ? __builtin_nontemporal_load(&x16[i + u * stride]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < kQuantUnroll; ++u)
-                if (i + u * stride < n16) store_codes(&q8[i + u * stride], quant8(v[u], s, r, exact_only));
+                if (i + u * stride < n16) store_codes<NT>(&q8[i + u * stride], quant8(v[u], s, r, exact_only));
         }
     }
     // the last numel % 8 elements, one per lane of workgroup 0
@@ -249,7 +263,8 @@ extern "C" int qvae_act_quantize(const uint16_t *x, int64_t numel, float clip_ra
     int64_t want = (n16 + (int64_t)kQuantThreads * kQuantUnroll - 1) / ((int64_t)kQuantThreads * kQuantUnroll);
     const int64_t cap = (int64_t)device_cus() * 8;
     const int blocks = (int)(want < 1 ? 1 : (want > cap ? cap : want));
-    hipLaunchKernelGGL(k_quantize, dim3(blocks), dim3(kQuantThreads), 0, as_stream(stream),
+    hipLaunchKernelGGL(numel >= kCachedCodesMin ? k_quantize<false> : k_quantize<true>, dim3(blocks),
+                       dim3(kQuantThreads), 0, as_stream(stream),
                        reinterpret_cast<const u32x4 *>(x), n16, x, numel, clip_ratio, absmax, x_scale,
                        reinterpret_cast<uint2 *>(xq), xq);
     return launch_status();
