@@ -67,16 +67,12 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const u32x4 *__restri
     const int64_t stride = (int64_t)gridDim.x * kAbsmaxThreads;
     int64_t i = (int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x;
     // every pass issues all of its (in-range) loads before it uses any, the
-    // last, partial pass included: one memory round trip per pass.  The loads
-    // take the default cache policy: the quantize pass reads x again right
-    // after, and finds part of it in the last-level cache (an absmax ->
-    // quantize -> conv step 1-4 % faster than with non-temporal loads at 6 to
-    // 100 M elements, the chunked decode step ~2 %)
+    // last, partial pass included: one memory round trip per pass
     for (; i < n16; i += kAbsmaxUnroll * stride) {
         u32x4 v[kAbsmaxUnroll];
 #pragma unroll
         for (int u = 0; u < kAbsmaxUnroll; ++u)
-            v[u] = (i + u * stride < n16) ? x16[i + u * stride] : u32x4{0u, 0u, 0u, 0u};
+            v[u] = (i + u * stride < n16) ? __builtin_nontemporal_load(&x16[i + u * stride]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int u = 0; u < kAbsmaxUnroll; ++u) {
             m = pk_absmax(m, v[u].x);
