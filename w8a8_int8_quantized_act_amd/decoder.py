@@ -32,10 +32,13 @@ import torch
 from . import ops
 
 TOP_CHANNELS = 384
-# Frames from which the runner quantizes x inside the conv: the HBM-bound
-# 96-channel top level (at 1024 x 1024, 132 us against 56 + 89 us for the
-# quantize pass and the conv); at 256x256 and 512x512 the two-step path with
-# the 16x16-tile conv is faster (81 against 15 + 63 us, 104 against 28 + 72).
+# Frames on which the decoder benchmark's "quantize in the conv" variant uses
+# the input-quantizing conv (the HBM-bound 96-channel top level).  The runner
+# itself quantizes with the quantize pass unless asked otherwise: at 96 @
+# 1024x1024 the input-quantizing conv takes 151-160 us against 142-150 us for
+# the quantize pass and the conv together (the pass leaves the codes in the
+# last-level cache for the conv), and the two-step path is faster still on
+# the smaller levels.
 QIN_MIN_PIXELS = 512 * 1024
 
 
@@ -99,8 +102,9 @@ class PlannedConv:
         self.name = name
         # W8A8 layers: quantize x inside the conv (absmax pass + the input-quantizing
         # conv) or with the quantize pass (absmax + quantize + conv).  None picks the
-        # former for frames with at least QIN_MIN_PIXELS pixels, where it measured
-        # faster; the results are identical.
+        # latter: with the quantize pass leaving large tensors' codes in the
+        # last-level cache for the conv, it measured at least as fast on every
+        # decoder level; the results are identical.
         self.quantize_in_conv = quantize_in_conv
         global _code_loaded
         if not _code_loaded:
@@ -126,9 +130,7 @@ class PlannedConv:
                 self.fallbacks += 1
 
     def uses_quantize_in_conv(self, x: torch.Tensor) -> bool:
-        if self.quantize_in_conv is not None:
-            return self.quantize_in_conv
-        return x.numel() // x.shape[-1] >= QIN_MIN_PIXELS
+        return bool(self.quantize_in_conv)
 
     def __call__(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         if self.w8a8:
